@@ -1,0 +1,22 @@
+"""CPU oracle for the quantized decode / routed-expert path.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import anything from this package.  The
+product (the HIP library and its Python binding) never calls it, and this
+package never imports the product.
+
+Everything here is a plain, slow, obviously correct restatement of what the
+path computes, in float64 NumPy:
+
+* ``oracle.formats``  -- the five block formats: quantizer, packer, unpacker,
+  exact dequantization (Q8_0, Q4_0, MXFP4, Q4_K, Q6_K).
+* ``oracle.moe``      -- dense quantized GEMV, router + softmax top-k,
+  expert permutation, expert FFN with SwiGLU, weighted combine, the whole
+  routed-expert layer, and the per-element error bounds used for parity.
+* ``oracle.brute``    -- pure-Python scalar loops for tiny cases, used only to
+  cross-check the vectorised oracle.
+
+Parity status: every public function is pinned by a CPU test in
+``tests/test_oracle_*.py`` (closed-form blocks, error bounds, brute force,
+invariants).  No function is "parity unpinned".
+"""
