@@ -123,8 +123,7 @@ def _safe_div(num, den):
     num = np.asarray(num, dtype=np.float64)
     den = np.broadcast_to(np.asarray(den, dtype=np.float64), num.shape)
     out = np.zeros(num.shape, dtype=np.float64)
-    nz = den != 0
-    out[nz] = num[nz] / den[nz]
+    np.divide(num, den, out=out, where=den != 0)
     return out
 
 
@@ -191,14 +190,14 @@ def quantize_mxfp4(W):
 
 def quantize_q4_k(W):
     """Per 32-value sub-block j: lo = min(0, min w), s_j = (max w - lo)/15,
-    m'_j = -lo.  d = fp16(max_j s_j / 63), dmin = fp16(max_j m'_j / 63),
+    m'_j = 0 - lo.  d = fp16(max_j s_j / 63), dmin = fp16(max_j m'_j / 63),
     sc_j = clamp(round(s_j/d), 0, 63), m_j = clamp(round(m'_j/dmin), 0, 63),
     q = clamp(round((w + dmin*m_j) / (d*sc_j)), 0, 15).  Non-iterative."""
     w, N, K = _as_blocks(W, 256)
     w = w.reshape(N, K // 256, 8, 32)
     lo = np.minimum(0.0, w.min(axis=-1))
     s = (w.max(axis=-1) - lo) / 15.0
-    mp = -lo
+    mp = 0.0 - lo                # +0 (not -0) when lo is 0: the sign of a zero is not data
     d16 = fp16_rne(s.max(axis=-1) / 63.0)
     dmin16 = fp16_rne(mp.max(axis=-1) / 63.0)
     d = d16.astype(np.float64)[..., None]
@@ -239,17 +238,27 @@ def _pack_nibbles(codes):
 
 
 def _pack_q4k_meta(d16, dmin16, sc, m):
-    """[N, nb] fp16 d, dmin and [N, nb, 8] 6-bit sc, m -> [N, nb, 16] bytes."""
+    """[N, nb] fp16 d, dmin and [N, nb, 8] 6-bit sc, m -> [N, nb, 16] bytes.
+    The 96-bit field is assembled as a low 64-bit word (bits 0..63) and a high
+    32-bit word (bits 64..95)."""
     N, nb = d16.shape
     out = np.zeros((N, nb, 16), dtype=np.uint8)
     out[..., 0:2] = d16.astype("<f2").view(np.uint8).reshape(N, nb, 2)
     out[..., 2:4] = dmin16.astype("<f2").view(np.uint8).reshape(N, nb, 2)
-    bits = np.zeros((N, nb, 96), dtype=np.uint8)
-    for j in range(8):
-        for b in range(6):
-            bits[..., 6 * j + b] = (sc[..., j] >> b) & 1
-            bits[..., 48 + 6 * j + b] = (m[..., j] >> b) & 1
-    out[..., 4:16] = np.packbits(bits, axis=-1, bitorder="little")
+    lo = np.zeros((N, nb), dtype=np.uint64)
+    hi = np.zeros((N, nb), dtype=np.uint64)
+    fields = [(sc[..., j], 6 * j) for j in range(8)] + [(m[..., j], 48 + 6 * j) for j in range(8)]
+    for val, pos in fields:
+        v = val.astype(np.uint64) & np.uint64(63)
+        if pos + 6 <= 64:
+            lo |= v << np.uint64(pos)
+        elif pos >= 64:
+            hi |= v << np.uint64(pos - 64)
+        else:                                   # straddles bit 64
+            lo |= (v << np.uint64(pos)) & np.uint64(0xFFFFFFFFFFFFFFFF)
+            hi |= v >> np.uint64(64 - pos)
+    out[..., 4:12] = lo.astype("<u8").view(np.uint8).reshape(N, nb, 8)
+    out[..., 12:16] = hi.astype("<u4").view(np.uint8).reshape(N, nb, 4)
     return out
 
 
@@ -285,10 +294,15 @@ def pack(fmt, fields, N, K):
     return buf
 
 
-def quantize(fmt, W):
-    """float32 [N, K] -> packed bytes (uint8, tensor_bytes(fmt, N, K))."""
-    N, K = np.asarray(W).shape
-    return pack(fmt, QUANTIZE[fmt](W), N, K)
+def quantize(fmt, W, rows_per_chunk=64):
+    """float32 [N, K] -> packed bytes (uint8, tensor_bytes(fmt, N, K)).
+    Blocks never span rows, so rows are quantized in chunks (for speed) and
+    the fields concatenated."""
+    W = np.asarray(W, dtype=np.float32)
+    N, K = W.shape
+    parts = [QUANTIZE[fmt](W[i:i + rows_per_chunk]) for i in range(0, max(N, 1), rows_per_chunk)]
+    fields = {k: np.concatenate([p[k] for p in parts], axis=0) for k in parts[0]}
+    return pack(fmt, fields, N, K)
 
 
 # ----------------------------------------------------------- unpacking -----
@@ -323,10 +337,22 @@ def unpack(fmt, buf, N, K):
         meta = p[1].reshape(N, nb, 16)
         d = meta[..., 0:2].copy().view("<f2").astype(np.float64)[..., 0]
         dmin = meta[..., 2:4].copy().view("<f2").astype(np.float64)[..., 0]
-        bits = np.unpackbits(meta[..., 4:16], axis=-1, bitorder="little")
-        weights = 1 << np.arange(6)
-        sc = np.stack([bits[..., 6 * j:6 * j + 6] @ weights for j in range(8)], -1)
-        m = np.stack([bits[..., 48 + 6 * j:54 + 6 * j] @ weights for j in range(8)], -1)
+        # the 96-bit field as integers: bit b of the field is bit b%8 of byte
+        # 4 + b//8; field(pos) = the 6 bits starting at pos
+        lo = meta[..., 4:12].copy().view("<u8")[..., 0].astype(np.uint64)
+        hi = meta[..., 12:16].copy().view("<u4")[..., 0].astype(np.uint64)
+
+        def field(pos):
+            if pos + 6 <= 64:
+                v = lo >> np.uint64(pos)
+            elif pos >= 64:
+                v = hi >> np.uint64(pos - 64)
+            else:
+                v = (lo >> np.uint64(pos)) | (hi << np.uint64(64 - pos))
+            return (v & np.uint64(63)).astype(np.int64)
+
+        sc = np.stack([field(6 * j) for j in range(8)], -1)
+        m = np.stack([field(48 + 6 * j) for j in range(8)], -1)
         return {"q": _nibble(p[0], N, K), "d": d, "dmin": dmin,
                 "sc": sc.astype(np.int64), "m": m.astype(np.int64)}
     if fmt == "q6_k":
