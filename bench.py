@@ -1,0 +1,225 @@
+"""Benchmark: routed-expert (MoE) quantized decode on one MI355X.
+
+One step = one pass of the whole decode path (moe_route -> moe_permute ->
+moe_ffn_tiered -> moe_combine) over three layer calls, the decode row counts
+the metric names:
+  * 1 row and 6 rows through the tiered 512-expert top-10 layer (hidden 2048,
+    FFN 640; Q6_K/Q8_0 hot, Q4_K/Q4_0 middle, MXFP4 tail; rank prior),
+  * 16 bf16 rows through the grouped 256-expert top-8 layer (hidden 7168,
+    FFN 2048, Q4_K) with its always-on Q8_0 shared expert.
+Weights are synthetic (seeded device normals packed by the library's own
+quantizer); every layer keeps several weight copies at distinct addresses and
+steps rotate through them, so each call streams its experts from HBM rather
+than from the 256 MB last-level cache; activations cycle through 256 distinct
+rows so the expert set changes from call to call.
+
+value = weight bytes streamed per step (router + each distinct selected
+expert, shared included) / wall time per step, in GB/s.
+
+Extra fields: tokens/s per row count, fraction of the 8 TB/s HBM peak, the
+roofline of the dominant kernel (ffn_gate_up) from per-launch HIP events
+inside the timed region, and the CPU oracle timed on a bounded sample.
+
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("weight-stream GB/s (% HBM peak) + MoE-layer tokens/s at 1/6/16 decode rows")
+HBM_PEAK_GBS = 8000.0
+POOL = 256
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def build_workload(torch):
+    from decode_moe_mul_amd import configs, layers, synth
+    t0 = time.time()
+    tiered = layers.MoELayer(configs.TIERED, copies=4)
+    log(f"tiered layer built ({time.time() - t0:.1f}s)")
+    t0 = time.time()
+    grouped = layers.MoELayer(configs.GROUPED, copies=2)
+    log(f"grouped layer built ({time.time() - t0:.1f}s)")
+    xt = torch.from_numpy(synth.normal((POOL, 2048), 1.0, 1, synth.ACT, 0)).cuda()
+    xg = torch.from_numpy(synth.bf16_round(synth.normal((POOL, 7168), 1.0, 1, synth.ACT, 1)))
+    xg = xg.cuda().to(torch.bfloat16)
+    return tiered, grouped, xt, xg
+
+
+def step_calls(tiered, grouped, xt, xg, s):
+    """The three layer calls of step s: (layer, x, copy, rows)."""
+    x1 = xt[s % POOL:s % POOL + 1]
+    o6 = (6 * s) % (POOL - 6)
+    x6 = xt[o6:o6 + 6]
+    o16 = (16 * s) % (POOL - 16)
+    x16 = xg[o16:o16 + 16]
+    return [(tiered, x1, s % 4, 1), (tiered, x6, (s + 2) % 4, 6), (grouped, x16, s % 2, 16)]
+
+
+def cpu_baseline(budget_s=20.0):
+    """The oracle (float64 NumPy) on the tiered layer at 1 row, on a bounded
+    sample of tokens: per token, dequantize-then-dot of its 10 experts and the
+    router.  Inputs are quantized by the oracle (untimed)."""
+    from decode_moe_mul_amd import configs, synth
+    from oracle import formats as fm
+    from oracle import moe
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    cfg = configs.TIERED
+    Wr = synth.normal((cfg.E, cfg.H), cfg.sigma_router, 0, synth.ROUTER, 0)
+    b = synth.rank_prior(cfg.E, cfg.prior_lambda)
+    x = synth.normal((64, cfg.H), 1.0, 2, synth.ACT, 0)
+    cache = {}
+
+    def expert(e):
+        if e not in cache:
+            t = cfg.tier_of(e)
+            w = [synth.normal((cfg.F, cfg.H), cfg.sigma_w, 0, tag, e) for tag in (synth.GATE, synth.UP)]
+            wd = synth.normal((cfg.H, cfg.F), cfg.sigma_w, 0, synth.DOWN, e)
+            cache[e] = (t.fmt_gate_up, fm.quantize(t.fmt_gate_up, w[0]),
+                        fm.quantize(t.fmt_gate_up, w[1]), t.fmt_down, fm.quantize(t.fmt_down, wd))
+        return cache[e]
+
+    def ebytes(e):
+        t = cfg.tier_of(e)
+        return 2 * fm.tensor_bytes(t.fmt_gate_up, cfg.F, cfg.H) + fm.tensor_bytes(t.fmt_down, cfg.H, cfg.F)
+
+    done, elapsed, nbytes = 0, 0.0, 0
+    for t in range(x.shape[0]):
+        ids, p, _ = moe.route(x[t:t + 1], Wr, b, cfg.k)       # untimed: quantize its experts
+        for e in ids[0]:
+            expert(int(e))
+        t0 = time.perf_counter()
+        ids, p, _ = moe.route(x[t:t + 1], Wr, b, cfg.k)
+        moe.moe_layer(x[t:t + 1], ids, p, expert, cfg.H, cfg.F, cfg.E)
+        elapsed += time.perf_counter() - t0
+        nbytes += cfg.E * cfg.H * 4 + sum(ebytes(int(e)) for e in np.unique(ids))
+        done += 1
+        if elapsed > budget_s:
+            break
+    return {"value": round(nbytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": int(blas_threads),
+            "kind": "oracle",
+            "sample": f"tiered 512-expert layer at 1 row, {done} tokens, float64 NumPy "
+                      f"dequantize-then-dot ({elapsed:.1f}s; {done / elapsed:.2f} tokens/s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    a = ap.parse_args()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; the decode path has "
+                                   "no multi-GPU mode (run with --gpus 1)"}))
+        sys.exit(2)
+
+    import torch
+    from decode_moe_mul_amd import qmoe
+
+    torch.cuda.set_device(0)
+    qmoe.lib()
+    tiered, grouped, xt, xg = build_workload(torch)
+    stream = torch.cuda.current_stream()
+
+    # algorithmic bytes per call (routing is deterministic: take it from one pass)
+    per_step_bytes, gate_up_bytes = [], []
+    for s in range(a.steps):
+        b_step, g_step = 0, 0
+        for layer, x, copy, rows in step_calls(tiered, grouped, xt, xg, s):
+            _, ws = layer.forward(x, copy)
+            ids = ws["ids"].cpu().numpy()
+            b_step += layer.weight_bytes(ids)
+            flat = np.unique(ids)
+            g_step += sum(2 * qmoe.tensor_bytes(layer.cfg.tier_of(int(e)).fmt_gate_up,
+                                                layer.cfg.F, layer.cfg.H) for e in flat)
+        per_step_bytes.append(b_step)
+        gate_up_bytes.append(g_step)
+
+    for s in range(a.warmup):
+        for layer, x, copy, rows in step_calls(tiered, grouped, xt, xg, s):
+            layer.forward(x, copy)
+    torch.cuda.synchronize()
+
+    # timed region: per-call events (for tokens/s per row count) and the
+    # library's per-launch events (for the dominant kernel's roofline)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(a.steps)]
+    qmoe.profile_reset()
+    qmoe.profile_enable(True)
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for s in range(a.steps):
+        ev[s][0].record(stream)
+        for i, (layer, x, copy, rows) in enumerate(step_calls(tiered, grouped, xt, xg, s)):
+            layer.forward(x, copy)
+            ev[s][i + 1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    qmoe.profile_enable(False)
+    total_ms = t_start.elapsed_time(t_end)
+    ms_step = total_ms / a.steps
+    call_ms = np.array([[ev[s][i].elapsed_time(ev[s][i + 1]) for i in range(3)]
+                        for s in range(a.steps)]).sum(axis=0)
+    n_gu, gu_ms = qmoe.profile_read("ffn_gate_up")
+    kernel_ms = {k: qmoe.profile_read(k) for k in
+                 ("router_gemv", "topk", "permute", "ffn_gate_up", "ffn_down", "combine")}
+
+    total_bytes = float(np.sum(per_step_bytes))
+    gbs = total_bytes / (total_ms * 1e-3) / 1e9
+    gu_gbs = float(np.sum(gate_up_bytes)) / (gu_ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "moe_decode_rows_1_6_16",
+                   "layers": {"rows_1_and_6": "tiered E=512 top-10 H=2048 F=640 "
+                                              "Q6_K/Q8_0 | Q4_K/Q4_0 | MXFP4, rank prior",
+                              "rows_16": "grouped E=256 top-8 H=7168 F=2048 Q4_K "
+                                         "+ Q8_0 shared, bf16 rows"},
+                   "weight_copies": {"tiered": 4, "grouped": 2}},
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "tokens_per_s": {str(r): round(r * a.steps / (call_ms[i] * 1e-3), 1)
+                         for i, r in enumerate((1, 6, 16))},
+        "ms_per_call": {str(r): round(call_ms[i] / a.steps, 5) for i, r in enumerate((1, 6, 16))},
+        "weight_bytes_per_step": int(total_bytes / a.steps),
+        "kernel_ms_per_step": {k: round(v[1] / a.steps, 5) for k, v in kernel_ms.items()},
+        "roofline": {"bound": "hbm", "kernel": "ffn_gate_up",
+                     "achieved": round(gu_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "launches": n_gu,
+                     "avg_launch_us": round(gu_ms * 1e3 / max(n_gu, 1), 3),
+                     "algorithmic_bytes_per_launch": int(np.sum(gate_up_bytes) / max(n_gu, 1))},
+    }
+    if not a.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

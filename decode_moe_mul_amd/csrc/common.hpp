@@ -1,0 +1,207 @@
+// Internal header of libqmoe: plane layout, number conversions, per-format
+// decoding of 32-value units, launch/error/profiling helpers.
+//
+// The value formulas are those of the block formats named on the "RTX 3090
+// Llama 70B three-tier cache" page (section 一) and the "Three RTX 3090
+// Qwen3.8-Flash-Next guide" page (section 优化策略二); the plane layout is this
+// library's own and is described in include/qmoe.h.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/qmoe.h"
+
+#define QMOE_HD __host__ __device__ __forceinline__
+#define QMOE_D __device__ __forceinline__
+
+namespace qmoe {
+
+// ------------------------------------------------------------- layout ----
+struct Layout {
+  size_t off[4];
+  size_t total;
+  int nplanes;
+};
+
+QMOE_HD size_t round_up256(size_t n) { return (n + 255) & ~size_t(255); }
+
+QMOE_HD int block_of(int fmt) {
+  return (fmt == QMOE_Q4_K || fmt == QMOE_Q6_K) ? 256
+         : (fmt >= QMOE_Q8_0 && fmt <= QMOE_MXFP4) ? 32
+                                                  : 0;
+}
+
+// Plane sizes per format, in storage order, for a [N, K] tensor.
+QMOE_HD Layout layout_of(int fmt, int N, int K) {
+  Layout L{};
+  const size_t n = (size_t)N, k = (size_t)K;
+  size_t sz[4] = {0, 0, 0, 0};
+  int np = 2;
+  switch (fmt) {
+    case QMOE_Q8_0: sz[0] = n * k; sz[1] = n * (k / 32) * 2; break;
+    case QMOE_Q4_0: sz[0] = n * k / 2; sz[1] = n * (k / 32) * 2; break;
+    case QMOE_MXFP4: sz[0] = n * k / 2; sz[1] = n * (k / 32); break;
+    case QMOE_Q4_K: sz[0] = n * k / 2; sz[1] = n * (k / 256) * 16; break;
+    case QMOE_Q6_K:
+      sz[0] = n * k / 2; sz[1] = n * k / 4; sz[2] = n * (k / 256) * 16;
+      sz[3] = n * (k / 256) * 2; np = 4; break;
+    default: np = 0;
+  }
+  size_t pos = 0;
+  for (int i = 0; i < np; ++i) {
+    L.off[i] = pos;
+    pos = round_up256(pos + sz[i]);
+  }
+  L.total = pos;
+  L.nplanes = np;
+  return L;
+}
+
+// ------------------------------------------------------- conversions ----
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+
+QMOE_D float f16_bits_to_f32(uint32_t bits16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+QMOE_D uint32_t f32_to_f16_bits(float v) {  // round to nearest even
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v);
+}
+QMOE_D uint32_t pack_h2(float lo, float hi) {
+  return f32_to_f16_bits(lo) | (f32_to_f16_bits(hi) << 16);
+}
+QMOE_D float bf16_bits_to_f32(uint32_t bits16) {
+  return __builtin_bit_cast(float, bits16 << 16);
+}
+QMOE_D uint32_t pk_add_h2(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2_t, a) + __builtin_bit_cast(h2_t, b));
+}
+QMOE_D uint32_t pk_mul_h2(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2_t, a) * __builtin_bit_cast(h2_t, b));
+}
+// sum over the pair: a.lo*b.lo + a.hi*b.hi + c, fp32 accumulate
+QMOE_D float fdot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, a), __builtin_bit_cast(h2_t, b), c, false);
+}
+// 2^(e-127) for an E8M0 byte; 255 is NaN; e = 0 is the fp32 subnormal 2^-127
+QMOE_D float e8m0_to_f32(uint32_t e) {
+  uint32_t bits = e == 255u ? 0x7FC00000u : (e == 0u ? 0x00400000u : (e << 23));
+  return __builtin_bit_cast(float, bits);
+}
+
+// Load an activation element (fp32 or raw bf16) as fp32.
+QMOE_D float load_act(const void* x, int dtype, size_t i) {
+  return dtype == QMOE_F32 ? ((const float*)x)[i]
+                           : bf16_bits_to_f32(((const uint16_t*)x)[i]);
+}
+
+// --------------------------------------------------- unit decoding ------
+// A "unit" is 32 consecutive values of one weight row.  Its codes are turned
+// into 16 words of two fp16 each, holding exact small integers (or exact E2M1
+// values), so that a unit's dot product with fp16 activations is 16
+// v_dot2_f32_f16 followed by one multiply with the unit's scale.
+//
+// Pair order.  4-bit codes: word c of the 16 code bytes holds elements
+// 8c..8c+7 as nibbles; pair 4c+j = elements (8c+j, 8c+j+4).  8-bit codes:
+// word c holds elements 4c..4c+3; pair 2c+j = elements (4c+j, 4c+j+2).  The
+// activations are staged in the same pair order ("nibble" / "byte" order).
+
+constexpr uint32_t H2_MAGIC = 0x64006400u;  // fp16 1024 in both halves
+constexpr uint32_t H2_NEG_1024 = 0xE400E400u;
+constexpr uint32_t H2_NEG_1032 = 0xE408E408u;  // -(1024 + 8)
+constexpr uint32_t H2_NEG_1056 = 0xE420E420u;  // -(1024 + 32)
+constexpr uint32_t H2_NEG_1152 = 0xE480E480u;  // -(1024 + 128)
+constexpr uint32_t H2_2P14 = 0x74007400u;      // 2^14
+
+// nibble codes + fp16 bias  ->  exact (code - bias) in fp16 pairs
+QMOE_D void nibbles_to_h2(const uint4 q, uint32_t neg_bias, uint32_t out[16]) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      out[4 * c + j] = pk_add_h2(((w[c] >> (4 * j)) & 0x000F000Fu) | H2_MAGIC, neg_bias);
+}
+
+// E2M1 codes -> exact E2M1 values in fp16 pairs.  (m << 9) read as fp16 is
+// E2M1(m) * 2^-14 for the 3-bit magnitude m (m = 1 lands on an fp16
+// subnormal), so one multiply by 2^14 gives the value exactly.
+QMOE_D void e2m1_to_h2(const uint4 q, uint32_t out[16]) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t v = w[c] >> (4 * j);
+      const uint32_t bits = ((v & 0x00070007u) << 9) | ((v & 0x00080008u) << 12);
+      out[4 * c + j] = pk_mul_h2(bits, H2_2P14);
+    }
+}
+
+// Q6_K: low nibbles + 2 high bits per element -> exact (q - 32)
+QMOE_D void q6_to_h2(const uint4 ql, const uint2 qh, uint32_t out[16]) {
+  const uint32_t w[4] = {ql.x, ql.y, ql.z, ql.w};
+  const uint32_t hw[4] = {qh.x & 0xFFFFu, qh.x >> 16, qh.y & 0xFFFFu, qh.y >> 16};
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    // element i of the 8 has its high bits at 2i; spread so that elements j
+    // and j+4 sit at bits 2j and 16+2j
+    const uint32_t hh = (hw[c] & 0xFFu) | ((hw[c] & 0xFF00u) << 8);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t lo = (w[c] >> (4 * j)) & 0x000F000Fu;
+      const uint32_t hi = ((hh >> (2 * j)) & 0x00030003u) << 4;
+      out[4 * c + j] = pk_add_h2(lo | hi | H2_MAGIC, H2_NEG_1056);
+    }
+  }
+}
+
+// Q8_0: signed bytes -> exact q in fp16 pairs (byte order)
+QMOE_D void bytes_to_h2(const uint4 a, const uint4 b, uint32_t out[16]) {
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const uint32_t u = w[c] ^ 0x80808080u;  // q + 128 as unsigned bytes
+    out[2 * c] = pk_add_h2((u & 0x00FF00FFu) | H2_MAGIC, H2_NEG_1152);
+    out[2 * c + 1] = pk_add_h2(((u >> 8) & 0x00FF00FFu) | H2_MAGIC, H2_NEG_1152);
+  }
+}
+
+// Position, within a unit's 32 values, of element i of pair p (i = 0, 1).
+QMOE_HD int pair_elem_nibble(int p, int i) { return 8 * (p >> 2) + (p & 3) + 4 * i; }
+QMOE_HD int pair_elem_byte(int p, int i) { return 4 * (p >> 1) + (p & 1) + 2 * i; }
+constexpr bool byte_order(int fmt) { return fmt == QMOE_Q8_0; }
+
+// ------------------------------------------------- wave reductions ------
+// Sum across aligned groups of G lanes (G a power of two <= 64).
+template <int G>
+QMOE_D float group_sum(float v) {
+#pragma unroll
+  for (int off = G / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+}  // namespace qmoe
+
+// ----------------------------------------------- host-side helpers ------
+// (implemented in api.hip)
+namespace qmoe {
+int fail(int status, const char* fmt, ...);   // records qmoe_last_error text
+int check_launch(const char* kernel);         // hipGetLastError -> status
+bool profiling_on();
+void profile_begin(const char* kernel, hipStream_t s);
+void profile_end(const char* kernel, hipStream_t s);
+int cu_count();
+}  // namespace qmoe
+
+// Launch with optional event timing and error check; returns a qmoe status.
+#define QMOE_LAUNCH(name, kernel, grid, block, lds, stream, ...)            \
+  ([&]() -> int {                                                            \
+    if (qmoe::profiling_on()) qmoe::profile_begin(name, stream);             \
+    hipLaunchKernelGGL(kernel, grid, block, lds, stream, __VA_ARGS__);       \
+    int st_ = qmoe::check_launch(name);                                      \
+    if (qmoe::profiling_on()) qmoe::profile_end(name, stream);               \
+    return st_;                                                              \
+  }())
+
+#define QMOE_ALIGNED(p, a) ((((uintptr_t)(p)) & ((a)-1)) == 0)

@@ -1,0 +1,240 @@
+/*
+ * qmoe.h -- C ABI of libqmoe.so: quantized-weight decode and routed-expert
+ * (mixture-of-experts) layer kernels for AMD MI355X (gfx950), in HIP.
+ *
+ * What the path computes comes from these pages (cited by title + section):
+ *  [P2] "三张 RTX 3090 显卡实现 Qwen3.8-Flash-Next 80 Token 每秒的高效推理优化指南"
+ *       (n1n.ai): a 512-expert, top-10 MoE layer ("瓶颈分析"); experts re-indexed
+ *       by selection frequency so a precision tier is a contiguous id range
+ *       ("优化策略一"); per-tier formats Q6_K/Q8_0, 4-bit, MXFP4 ("优化策略二");
+ *       the routed matmul skips ids outside a tier's [min, max) range
+ *       ("优化策略三", kernel k_mul_mat_id_tiered); -1 skip sentinels must never
+ *       be dereferenced and gate/up/activation are fused in decode
+ *       ("关键 Bug 修复与调试踩坑记录", items 1, 3, 4).
+ *  [P3] "一张 RTX 3090 跑 Llama 70B：三层流式缓存 + NVMe 直连，速度干到 83 倍":
+ *       GGUF formats Q4_0, Q8_0, Q4_K, Q6_K (section 一); hand-written GEMV for
+ *       single-token decode and SwiGLU fused with the FC (section 4.4).
+ *  [P4] "多卡 CUDA 张量并行DwarfStar 如何在 8 张 L40S 上跑出 120 t/s": one kernel
+ *       launch serves 16 sessions' decode rows over Q4_K routed experts, with
+ *       a Q8 shared expert; prefill in 2048-token chunks
+ *       ("120 t/s 的秘密微批次分组解码", "快速上手").
+ *  [P1] "RTX 4080 SUPER 原生 Windows 跑 27B:NInfer 80 SM 移植实录": launch
+ *       geometry must follow the device's compute-unit count (sections 三, 四);
+ *       a bad memory plan must fail up front, not mid-run (section 五).
+ *
+ * Conventions (every entry point):
+ *  - All tensor arguments are DEVICE pointers owned by the caller.  The library
+ *    never allocates, frees or keeps caller memory.  Scratch space is a
+ *    caller-provided device workspace of at least *_workspace_size() bytes.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Calls
+ *    only enqueue work: no host synchronisation, no allocation, no memset, so
+ *    they may be captured in a HIP graph.
+ *  - Return 0 (QMOE_OK) or a negative qmoe_status.  All argument checks run on
+ *    the host before anything is launched; a failed call launches nothing.
+ *    qmoe_last_error() gives the detail text of the calling thread's last
+ *    failure.
+ *  - Sizes are int; a row count of 0 is a valid no-op.  Matrices are
+ *    row-major.  Activations are fp32 (QMOE_F32) or bf16 (QMOE_BF16, raw
+ *    uint16 storage); outputs are fp32.
+ *  - Quantized weight tensors use the plane layout below.  Weight and
+ *    workspace pointers must be 256-byte aligned; activation/output pointers
+ *    16-byte aligned.
+ *  - Device-side routing ids outside [0, E) (including the -1 sentinel) are
+ *    skipped: they contribute nothing and index nothing.
+ *  - Determinism: no floating-point atomics; repeated calls on the same
+ *    inputs give bit-identical results.
+ *
+ * Weight layout ("planes").  W[N, K] is quantized along K in blocks of B
+ * values (nb = K / B per row).  Each per-block field is a plane, row-major
+ * [N][nb][field bytes]; planes follow in the order listed, each starting at a
+ * 256-byte aligned offset; qmoe_tensor_bytes() gives the total.
+ *   Q8_0  B=32  : q int8[32]; d fp16.                      value d*q
+ *   Q4_0  B=32  : q 4-bit[32]; d fp16.                     value d*(q-8)
+ *   MXFP4 B=32  : q E2M1[32]; e uint8 (E8M0).              value 2^(e-127)*E2M1(q)
+ *   Q4_K  B=256 : q 4-bit[256]; meta 16 B = fp16 d, fp16 dmin, 96-bit LE field
+ *                 with sc_j at bits 6j.., m_j at bits 48+6j.. (j=0..7, 32-value
+ *                 sub-blocks).                             value d*sc_j*q - dmin*m_j
+ *   Q6_K  B=256 : ql 4-bit[256]; qh 2-bit[256]; sc int8[16]; d fp16 (16-value
+ *                 sub-blocks).                             value d*sc_j*(q-32)
+ *   4-bit element i of a row: byte i>>1, low nibble for even i.  Q6_K high
+ *   bits of element i: byte i>>2, bits 2*(i&3).  E2M1: bit3 sign, bits 2-1
+ *   exponent, bit 0 mantissa, magnitudes {0,.5,1,1.5,2,3,4,6} (OCP MX v1.0).
+ */
+#ifndef QMOE_H
+#define QMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QMOE_ABI_VERSION 1
+#define QMOE_MAX_TIERS 8
+
+typedef enum {
+  QMOE_OK = 0,
+  QMOE_ERR_INVALID_ARG = -1, /* null pointer, bad size, misalignment, k > E ... */
+  QMOE_ERR_UNSUPPORTED = -2, /* unknown format or dtype, size beyond a limit  */
+  QMOE_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required    */
+  QMOE_ERR_HIP = -4          /* the HIP runtime reported an error             */
+} qmoe_status;
+
+typedef enum {
+  QMOE_Q8_0 = 0,
+  QMOE_Q4_0 = 1,
+  QMOE_MXFP4 = 2,
+  QMOE_Q4_K = 3,
+  QMOE_Q6_K = 4
+} qmoe_format;
+
+typedef enum { QMOE_F32 = 0, QMOE_BF16 = 1 } qmoe_dtype;
+
+/* ---------------------------------------------------------------- meta -- */
+int qmoe_abi_version(void);
+const char *qmoe_status_string(int status);
+/* Detail text of the calling thread's most recent failing call ("" if none). */
+const char *qmoe_last_error(void);
+/* Block size B of a format (32 or 256), or 0 for an unknown format. */
+int qmoe_block_size(int fmt);
+/* Bytes of a packed [N, K] tensor; 0 if fmt is unknown or K % B != 0. */
+size_t qmoe_tensor_bytes(int fmt, int N, int K);
+/* Byte offset of each plane of a packed [N, K] tensor (up to 4 planes).
+ * Returns the number of planes, or a negative status. */
+int qmoe_plane_offsets(int fmt, int N, int K, size_t offsets[4]);
+/* Compute units of the current device (the launch geometry is sized from it). */
+int qmoe_device_cu_count(void);
+
+/* ---------------------------------------------------- block formats ----
+ * qquantize_<fmt>: w [N, K] fp32 -> packed tensor `out` (qmoe_tensor_bytes
+ *   bytes).  Quantization rule per block (float64 arithmetic on the fp32
+ *   inputs; scales rounded to fp16 nearest-even; codes against the stored
+ *   scale; code rounding half away from zero, then clamped; zero divisor ->
+ *   code offset only):
+ *     Q8_0 : d = fp16(max|w|/127); q = clamp(round(w/d), -127, 127)
+ *     Q4_0 : d = fp16(max|w|/7);   q = clamp(round(w/d) + 8, 0, 15)
+ *     MXFP4: e = clamp(127 + floor(log2 max|w|) - 2, 0, 254) (0 for an
+ *            all-zero block); codes = E2M1 round-to-nearest-even of
+ *            w / 2^(e-127), saturating at 6; sign bit = (w < 0)
+ *     Q4_K : per 32-sub-block lo = min(0, min w), s = (max w - lo)/15,
+ *            m' = 0 - lo; d = fp16(max s/63), dmin = fp16(max m'/63),
+ *            sc = clamp(round(s/d),0,63), m = clamp(round(m'/dmin),0,63),
+ *            q = clamp(round((w + dmin*m)/(d*sc)), 0, 15)
+ *     Q6_K : per 16-sub-block s = max|w|/31; d = fp16(max s/127),
+ *            sc = clamp(round(s/d),-128,127), q = clamp(round(w/(d*sc))+32,0,63)
+ *   (the offline per-tier packing of [P2] "优化策略二", done on the device).
+ * qdequant_<fmt>: packed [N, K] -> out [N, K] fp32, each value the exact
+ *   format value rounded to nearest-even fp32 (bit-exact reference decoder).
+ * qgemv_<fmt>: y[r, n] = sum_k deq(W)[n, k] * x[r, k] for r < R, n < N
+ *   ([P3] section 4.4 GEMV operator).  x is [R, K] of x_dtype, y is [R, N]
+ *   fp32.  R >= 0 (R rows share one pass over W).  Activations are rounded to
+ *   fp16 inside the dot product: |x| must stay below 65504.
+ * Errors: INVALID_ARG for null pointers, N or K < 0, K % B != 0, K > 65536,
+ *   misalignment; UNSUPPORTED for an unknown x_dtype.                      */
+#define QMOE_DECLARE_FORMAT(F)                                                 \
+  int qquantize_##F(const float *w, int N, int K, void *out, void *stream);    \
+  int qdequant_##F(const void *W, int N, int K, float *out, void *stream);     \
+  int qgemv_##F(const void *W, int N, int K, const void *x, int x_dtype, int R, \
+                float *y, void *stream);
+QMOE_DECLARE_FORMAT(q8_0)
+QMOE_DECLARE_FORMAT(q4_0)
+QMOE_DECLARE_FORMAT(mxfp4)
+QMOE_DECLARE_FORMAT(q4_k)
+QMOE_DECLARE_FORMAT(q6_k)
+#undef QMOE_DECLARE_FORMAT
+
+/* ----------------------------------------------------------- routing ----
+ * moe_route ([P2] "瓶颈分析": a light router picks the top-k of E experts per
+ * token):
+ *   logits[t, e] = sum_h x[t, h] * Wr[e, h] + bias[e]   (fp32 accumulation)
+ *   ids[t, 0..k-1] = the k largest logits, descending, ties to the lower id
+ *                    (NaN ranks below every number)
+ *   p[t, i] = exp(l_i - l_0) / sum_j exp(l_j - l_0) over the kept k
+ *   ids[t, k+s] = E + s and p[t, k+s] = 1 for s < n_shared (always-on shared
+ *   experts, [P4] "快速上手": Q8 shared expert)
+ * x [T, H] (x_dtype), Wr [E, H] fp32, bias [E] fp32 or NULL, ids/p
+ * [T, k+n_shared] int32/fp32, logits [T, E] fp32 or NULL (written when given).
+ * Limits: 1 <= k <= min(E, 64), E <= 4096, n_shared >= 0.
+ * Workspace: moe_route_workspace_size(T, H, E) bytes.                       */
+size_t moe_route_workspace_size(int T, int H, int E);
+int moe_route(const void *x, int x_dtype, int T, int H, const float *Wr,
+              const float *bias, int E, int k, int n_shared, int32_t *ids,
+              float *p, float *logits, void *ws, size_t ws_bytes, void *stream);
+
+/* moe_permute: stable counting sort of the flat assignments a = t*k + i by
+ * expert id ([P2] "优化策略三" groups a layer's routed tokens by expert; bug
+ * item 1 shows grouping must survive duplicate ids).
+ *   offsets[e] = number of valid assignments with id < e, e = 0..E
+ *   perm[pos]  = a, in ascending a within each expert, for pos < offsets[E];
+ *                -1 for pos >= offsets[E]
+ *   inv_perm[a] = pos, or -1 when ids[a] is outside [0, E)
+ * ids [T*k] int32 (any values); offsets [E+1], perm [T*k], inv_perm [T*k].
+ * Limits: E <= 8192, T*k <= 1<<24.  No workspace.                           */
+int moe_permute(const int32_t *ids, int T, int k, int E, int32_t *offsets,
+                int32_t *perm, int32_t *inv_perm, void *stream);
+
+/* ------------------------------------------------------- expert FFN ----
+ * A tier is a contiguous expert-id range with one format for gate/up and one
+ * for down ([P2] "优化策略二", "优化策略三").  Its experts are stored back to
+ * back: expert e's gate tensor [F, H] starts at
+ *   gate + (e - e_begin) * qmoe_tensor_bytes(fmt_gate_up, F, H),
+ * and likewise up [F, H] and down [H, F] (stride qmoe_tensor_bytes(fmt_down,
+ * H, F)).  Tiers must be disjoint; together they cover [0, E).               */
+typedef struct qmoe_tier {
+  int32_t e_begin, e_end; /* expert ids [e_begin, e_end)        */
+  int32_t fmt_gate_up;    /* qmoe_format of gate and up [F, H]  */
+  int32_t fmt_down;       /* qmoe_format of down [H, F]         */
+  const void *gate, *up, *down;
+} qmoe_tier;
+
+/* moe_ffn_tiered (decode rows): for every valid permuted position pos
+ * (pos < offsets[E]) with expert e and token t = perm[pos] / k:
+ *   g = deq(Wg_e) x_t,  u = deq(Wu_e) x_t,  h = g / (1 + exp(-g)) * u,
+ *   o[pos, :] = deq(Wd_e) h                                (fp32 [T*k, H])
+ * ([P2] bug item 4: gate, up and activation fused; [P3] 4.4: SwiGLU fused).
+ * All tiers run in the same launches; rows o[pos] for pos >= offsets[E] are
+ * not written.  offsets/perm are moe_permute's.  x as in moe_route; |x| and
+ * |h| must stay below 65504 (fp16 inside the dot products).
+ * Limits: n_tiers <= QMOE_MAX_TIERS; H, F <= 65536.
+ * Workspace: moe_ffn_workspace_size(T, k, F) bytes.                         */
+size_t moe_ffn_workspace_size(int T, int k, int F);
+int moe_ffn_tiered(const qmoe_tier *tiers, int n_tiers, int E, int H, int F,
+                   const void *x, int x_dtype, int T, int k,
+                   const int32_t *offsets, const int32_t *perm, float *o,
+                   void *ws, size_t ws_bytes, void *stream);
+
+/* qgemm_grouped_prefill: the same result as moe_ffn_tiered for long chunks
+ * (a 2048-token prefill chunk, [P4] "120 t/s 的秘密微批次分组解码"): per
+ * expert, weight tiles are dequantized to bf16 and multiplied on the matrix
+ * cores with fp32 accumulation; activations are rounded to bf16 and h is
+ * stored as bf16 between the two passes.  Same arguments as moe_ffn_tiered.
+ * Workspace: qgemm_grouped_prefill_workspace_size(T, k, E, F) bytes.        */
+size_t qgemm_grouped_prefill_workspace_size(int T, int k, int E, int F);
+int qgemm_grouped_prefill(const qmoe_tier *tiers, int n_tiers, int E, int H,
+                          int F, const void *x, int x_dtype, int T, int k,
+                          const int32_t *offsets, const int32_t *perm, float *o,
+                          void *ws, size_t ws_bytes, void *stream);
+
+/* moe_combine: y[t, :] = sum_{i<k} p[t, i] * o[inv_perm[t*k + i], :]
+ *                        + shared[t, :]
+ * summed in slot order i = 0..k-1 (slots with inv_perm < 0 skipped), shared
+ * added last when not NULL ([P2] "瓶颈分析": weighted sum of the selected
+ * experts).  o [*, H] fp32 (permuted rows), p [T, k] fp32, y [T, H] fp32.
+ * Limit: H % 4 == 0.                                                         */
+int moe_combine(const float *o, const int32_t *inv_perm, const float *p, int T,
+                int k, int H, const float *shared, float *y, void *stream);
+
+/* ----------------------------------------------------------- profiling --
+ * Optional per-kernel timing with HIP events recorded around every launch the
+ * library makes while enabled (on the launch stream).  qmoe_profile_read
+ * waits for the recorded events and returns, for the kernel named `name`,
+ * the number of launches and their summed duration in milliseconds.         */
+int qmoe_profile_enable(int on);
+int qmoe_profile_reset(void);
+int qmoe_profile_read(const char *name, int *launches, double *total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QMOE_H */

@@ -1,0 +1,125 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry point
+include/qmoe.h declares, sizes its tensors as the oracle's layout does, and
+rejects bad arguments on the host before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from oracle import formats as fm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qmoe.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = set(re.findall(r"^\s*(?:const\s+)?(?:int|size_t|char\s*\*|const char\s*\*)\s*\*?\s*(\w+)\s*\(",
+                           text, flags=re.M))
+    for fmt in fm.FORMATS:
+        names |= {f"qquantize_{fmt}", f"qdequant_{fmt}", f"qgemv_{fmt}"}
+    names.discard("QMOE_DECLARE_FORMAT")
+    return sorted(names)
+
+
+@pytest.fixture(scope="module")
+def L():
+    from decode_moe_mul_amd import qmoe
+    return qmoe.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared()
+    assert len(names) >= 30
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_abi_version_and_strings(L):
+    assert L.qmoe_abi_version() == 1
+    assert L.qmoe_status_string(0) == b"ok"
+    assert L.qmoe_status_string(-3) == b"workspace too small"
+
+
+@pytest.mark.parametrize("fmt", fm.FORMATS)
+@pytest.mark.parametrize("N,K", [(1, 256), (640, 2048), (2048, 640), (14336, 4096), (7, 512)])
+def test_tensor_bytes_matches_oracle_layout(L, fmt, N, K):
+    from decode_moe_mul_amd import qmoe
+    if K % fm.BLOCK[fmt]:
+        assert L.qmoe_tensor_bytes(qmoe.FORMATS[fmt], N, K) == 0
+        return
+    assert L.qmoe_tensor_bytes(qmoe.FORMATS[fmt], N, K) == fm.tensor_bytes(fmt, N, K)
+    assert qmoe.plane_offsets(fmt, N, K) == fm.plane_offsets(fmt, N, K)[0]
+
+
+def test_block_sizes(L):
+    assert [L.qmoe_block_size(i) for i in range(5)] == [32, 32, 32, 256, 256]
+    assert L.qmoe_block_size(7) == 0
+
+
+def test_host_validation_rejects_before_launch(L):
+    from decode_moe_mul_amd import qmoe
+    fake = ctypes.c_void_p(256 * 1000)  # never dereferenced: every call below fails validation
+    # K not a multiple of the block
+    assert L.qgemv_q4_k(fake, 4, 100, fake, 0, 1, fake, None) == -1
+    # unknown activation dtype
+    assert L.qgemv_q8_0(fake, 4, 64, fake, 7, 1, fake, None) == -2
+    # null pointers
+    assert L.qgemv_q8_0(None, 4, 64, fake, 0, 1, fake, None) == -1
+    # misaligned weights
+    assert L.qgemv_q8_0(ctypes.c_void_p(256 * 1000 + 4), 4, 64, fake, 0, 1, fake, None) == -1
+    # router: k > E, k > 64, E too large
+    assert L.moe_route(fake, 0, 4, 64, fake, None, 8, 9, 0, fake, fake, None, fake, 1 << 20, None) == -1
+    assert L.moe_route(fake, 0, 4, 64, fake, None, 8192, 4, 0, fake, fake, None, fake, 1 << 30, None) == -2
+    # router: workspace too small
+    need = L.moe_route_workspace_size(4, 64, 16)
+    assert need > 0
+    assert L.moe_route(fake, 0, 4, 64, fake, None, 16, 2, 0, fake, fake, None, fake, need - 1, None) == -3
+    # permute: E too large
+    assert L.moe_permute(fake, 4, 2, 9000, fake, fake, fake, None) == -2
+    # combine: H not a multiple of 4
+    assert L.moe_combine(fake, fake, fake, 4, 2, 6, None, fake, None) == -1
+    # tiers that do not cover [0, E)
+    tier = qmoe.Tier(0, 4, 0, 0, 256 * 1000, 256 * 1000, 256 * 1000)
+    arr = (qmoe.Tier * 1)(tier)
+    ws_need = L.moe_ffn_workspace_size(2, 2, 64)
+    assert L.moe_ffn_tiered(arr, 1, 8, 64, 64, fake, 0, 2, 2, fake, fake, fake, fake,
+                            ws_need, None) == -1
+    assert b"cover" in L.qmoe_last_error()
+    # overlapping tiers
+    arr2 = (qmoe.Tier * 2)(qmoe.Tier(0, 4, 0, 0, 256000, 256000, 256000),
+                           qmoe.Tier(3, 8, 0, 0, 256000, 256000, 256000))
+    assert L.moe_ffn_tiered(arr2, 2, 8, 64, 64, fake, 0, 2, 2, fake, fake, fake, fake,
+                            ws_need, None) == -1
+    # unknown format in a tier
+    arr3 = (qmoe.Tier * 1)(qmoe.Tier(0, 8, 9, 0, 256000, 256000, 256000))
+    assert L.moe_ffn_tiered(arr3, 1, 8, 64, 64, fake, 0, 2, 2, fake, fake, fake, fake,
+                            ws_need, None) == -2
+    # workspace too small
+    arr4 = (qmoe.Tier * 1)(qmoe.Tier(0, 8, 0, 0, 256000, 256000, 256000))
+    assert L.moe_ffn_tiered(arr4, 1, 8, 64, 64, fake, 0, 2, 2, fake, fake, fake, fake,
+                            ws_need - 1, None) == -3
+    assert L.qgemm_grouped_prefill(arr4, 1, 8, 64, 64, fake, 0, 2, 2, fake, fake, fake, fake,
+                                   16, None) == -3
+
+
+def test_zero_rows_are_noops(L):
+    fake = ctypes.c_void_p(256 * 1000)
+    assert L.qgemv_q8_0(fake, 0, 64, fake, 0, 1, fake, None) == 0
+    assert L.qgemv_q8_0(fake, 4, 64, fake, 0, 0, fake, None) == 0
+    assert L.moe_route(fake, 0, 0, 64, fake, None, 16, 2, 0, fake, fake, None, None, 0, None) == 0
+    assert L.moe_combine(None, None, None, 0, 2, 64, None, fake, None) == 0
+    arr = (ctypes.c_byte * 1)()
+    from decode_moe_mul_amd import qmoe
+    t = (qmoe.Tier * 1)(qmoe.Tier(0, 8, 0, 0, 256000, 256000, 256000))
+    assert L.moe_ffn_tiered(t, 1, 8, 64, 64, fake, 0, 0, 2, fake, fake, fake, None, 0, None) == 0
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    from decode_moe_mul_amd import qmoe
+    monkeypatch.setattr(qmoe, "_lib", None)
+    monkeypatch.setattr(qmoe, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(qmoe.QmoeError):
+        qmoe.lib()
