@@ -167,10 +167,86 @@ QMOE_D void bytes_to_h2(const uint4 a, const uint4 b, uint32_t out[16]) {
   }
 }
 
+// ---- biased codes (dot-product path) ----------------------------------
+// The same magic-number decode without the bias subtraction: the fp16 code
+// words hold bias + code exactly, and the unit's dot product with the staged
+// activations carries bias * (their sum), which the staging computes once per
+// unit and the dot subtracts.  In the 4- and 6-bit formats the codes of odd
+// pair index j are taken four bits up (fp16 1024 + 16 * code), which needs no
+// shift; the activations of those pairs are staged divided by 16.
+
+// Q4_0 / Q4_K nibbles: pair 4c+j = (1024 + e, 1024 + e') for even j and
+// (1024 + 16e, 1024 + 16e') for odd j, e = element 8c+j, e' = element 8c+j+4.
+QMOE_D void nibbles_biased(const uint4 q, uint32_t out[16]) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const uint32_t t = w[c] >> 8;
+    out[4 * c + 0] = (w[c] & 0x000F000Fu) | H2_MAGIC;
+    out[4 * c + 1] = (w[c] & 0x00F000F0u) | H2_MAGIC;
+    out[4 * c + 2] = (t & 0x000F000Fu) | H2_MAGIC;
+    out[4 * c + 3] = (t & 0x00F000F0u) | H2_MAGIC;
+  }
+}
+
+// Q6_K: the unsigned 6-bit code (low nibble + 2 high bits) in the same
+// positions: 1024 + q (even j) or 1024 + 16 q (odd j), q in [0, 63].
+QMOE_D void q6_biased(const uint4 ql, const uint2 qh, uint32_t out[16]) {
+  const uint32_t w[4] = {ql.x, ql.y, ql.z, ql.w};
+  const uint32_t hw[4] = {qh.x & 0xFFFFu, qh.x >> 16, qh.y & 0xFFFFu, qh.y >> 16};
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    // high bits of elements 8c+j and 8c+j+4 at bits 2j and 16+2j
+    const uint32_t hh = (hw[c] & 0xFFu) | ((hw[c] & 0xFF00u) << 8);
+    const uint32_t t = w[c] >> 8;
+    out[4 * c + 0] = (w[c] & 0x000F000Fu) | ((hh << 4) & 0x00300030u) | H2_MAGIC;
+    out[4 * c + 1] = (w[c] & 0x00F000F0u) | ((hh << 6) & 0x03000300u) | H2_MAGIC;
+    out[4 * c + 2] = (t & 0x000F000Fu) | (hh & 0x00300030u) | H2_MAGIC;
+    out[4 * c + 3] = (t & 0x00F000F0u) | ((hh << 2) & 0x03000300u) | H2_MAGIC;
+  }
+}
+
+// Q8_0 (byte order): 1152 + q for the signed byte q.
+QMOE_D void bytes_biased(const uint4 a, const uint4 b, uint32_t out[16]) {
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const uint32_t u = w[c] ^ 0x80808080u;
+    out[2 * c] = (u & 0x00FF00FFu) | H2_MAGIC;
+    out[2 * c + 1] = ((u >> 8) & 0x00FF00FFu) | H2_MAGIC;
+  }
+}
+
+// MXFP4 in natural pair order (elements 2p, 2p+1): the exact E2M1 values,
+// one hardware conversion per byte (scale 1).
+QMOE_D void e2m1_natural(const uint4 q, uint32_t out[16]) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    out[4 * c + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[c], 1.f, 0));
+    out[4 * c + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[c], 1.f, 1));
+    out[4 * c + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[c], 1.f, 2));
+    out[4 * c + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[c], 1.f, 3));
+  }
+}
+
 // Position, within a unit's 32 values, of element i of pair p (i = 0, 1).
 QMOE_HD int pair_elem_nibble(int p, int i) { return 8 * (p >> 2) + (p & 3) + 4 * i; }
 QMOE_HD int pair_elem_byte(int p, int i) { return 4 * (p >> 1) + (p & 1) + 2 * i; }
 constexpr bool byte_order(int fmt) { return fmt == QMOE_Q8_0; }
+
+// Pair order of the biased codes: element of member i of pair p, and whether
+// the pair's codes sit four bits up (activations staged divided by 16).
+template <int FMT>
+QMOE_HD int pair_elem_biased(int p, int i) {
+  if constexpr (FMT == QMOE_Q8_0) return pair_elem_byte(p, i);
+  else if constexpr (FMT == QMOE_MXFP4) return 2 * p + i;
+  else return pair_elem_nibble(p, i);
+}
+template <int FMT>
+QMOE_HD bool pair_up4(int p) {
+  return (FMT == QMOE_Q4_0 || FMT == QMOE_Q4_K || FMT == QMOE_Q6_K) && (p & 1);
+}
 
 // ------------------------------------------------- wave reductions ------
 // Sum across aligned groups of G lanes (G a power of two <= 64).

@@ -4,27 +4,44 @@
 // guide" sections 优化策略二/三 and bug item 4; many session rows per launch,
 // [P4] "DwarfStar on 8x L40S" section "120 t/s 的秘密微批次分组解码").
 //
-// Work decomposition (one block = 4 waves):
-//  * a weight row is reduced by G lanes (G = largest power of two <= 64 that
-//    divides the row's 32-value unit count), so every lane owns whole
-//    32-value units and a wave covers 64/G rows;
-//  * each lane streams its units straight from HBM (16 B of codes per unit
-//    for 4-bit formats), decodes them to exact fp16 pairs and dots them with
-//    activations staged once per block in LDS (fp16, in the format's pair
-//    order); the unit scale is applied once per unit in fp32;
-//  * the rows of a token chunk (up to 16 rows) share one pass over the
-//    weights; longer row lists loop over chunks;
-//  * gate and up rows of the same output are computed by the same lanes, so
+// Decode is a weight stream: every weight byte is read once per call and
+// meets only a few activation rows, so the kernel is organised around HBM
+// streaming.
+//  * Schedule.  One launch per phase.  Block b serves (rank b / ntiles, row
+//    tile b % ntiles).  Every block ranks the experts that received rows
+//    (from the permutation offsets, staged in LDS): experts with more rows
+//    than the register blocking RC come first, then the others, so blocks
+//    are never wasted on empty experts and the heavy ones start first.
+//  * Few rows (<= RC, the common case): fp16 dot products.  The expert's
+//    activation rows are staged once per block in LDS (fp16, in the weight
+//    format's pair order, in a bank-conflict-free padded layout).  A weight
+//    row is reduced by G lanes (G a power of two, every lane owning >= 4
+//    whole 32-value units); a wave covers 64/G rows at a time.  Each lane
+//    streams its (row, unit) sequence through a 3-4 deep load pipeline that
+//    runs across row boundaries, decodes each unit once to exact fp16 pairs,
+//    and dots it against all staged rows with v_dot2_f32_f16; the unit scale
+//    is applied once per unit in fp32; row sums are reduced with DPP.
+//  * Many rows (a shared expert that sees every session row): the same row
+//    tile runs on the matrix cores, 16 rows at a time, fp16 operands
+//    dequantized in registers, v_mfma_f32_16x16x32_f16.
+//  * Gate and up rows of the same output are handled by the same lanes, so
 //    SiLU(g) * u is applied in registers before anything is stored.
 #include "common.hpp"
+#include "dequant.hpp"
+
+// Every fused multiply-add below is written out (fmaf); nothing else is
+// contracted, so a row's arithmetic does not depend on which register slot
+// (row position within a chunk) it occupies.
+#pragma clang fp contract(off)
 
 namespace qmoe {
 
 constexpr int kWaves = 4;
 constexpr int kBlock = 64 * kWaves;
-constexpr int kXCap = 16384;  // fp16 activation values staged per block
+constexpr int kLdsCap = 65536 - 256;
 
 struct Mat {
+  const uint8_t* base;
   const uint8_t* p0;
   const uint8_t* p1;
   const uint8_t* p2;
@@ -34,131 +51,192 @@ struct Mat {
 QMOE_D Mat mat_of(const void* base, int fmt, int N, int K) {
   const Layout L = layout_of(fmt, N, K);
   const uint8_t* b = (const uint8_t*)base;
-  return {b + L.off[0], b + L.off[1], b + L.off[2], b + L.off[3]};
+  return {b, b + L.off[0], b + L.off[1], b + L.off[2], b + L.off[3]};
 }
 
-// Load unit u (values 32u..32u+31) of row `row` and decode it: 16 fp16-pair
-// code words plus the fp32 coefficients of the unit.
+// ---------------------------------------------------- one 32-value unit --
+// Raw bytes of unit u of one weight row (loaded early), and its decode into
+// 16 fp16-pair code words plus fp32 coefficients:
 //   Q8_0/Q4_0/MXFP4: value = c0 * code
-//   Q4_K: value = c0 * code - c1          (c1 multiplies the sum of x)
-//   Q6_K: value = c0 * code (first 16), c1 * code (last 16)
+//   Q4_K:            value = c0 * code - c1   (c1 multiplies the sum of x)
+//   Q6_K:            value = c0 * code (values 0..15), c1 * code (16..31)
 template <int FMT>
-QMOE_D void load_unit(const Mat& M, int row, int u, int K, uint32_t codes[16], float& c0,
-                      float& c1) {
-  const size_t nb32 = (size_t)(K >> 5);
-  if constexpr (FMT == QMOE_Q8_0) {
-    const uint4* q = (const uint4*)(M.p0 + (size_t)row * K + 32 * (size_t)u);
-    const uint4 a = q[0], b = q[1];
-    const uint32_t d = ((const uint16_t*)M.p1)[row * nb32 + u];
-    bytes_to_h2(a, b, codes);
-    c0 = f16_bits_to_f32(d);
-    c1 = 0.f;
-  } else if constexpr (FMT == QMOE_Q4_0) {
-    const uint4 q = *(const uint4*)(M.p0 + (size_t)row * (K >> 1) + 16 * (size_t)u);
-    const uint32_t d = ((const uint16_t*)M.p1)[row * nb32 + u];
-    nibbles_to_h2(q, H2_NEG_1032, codes);
-    c0 = f16_bits_to_f32(d);
-    c1 = 0.f;
-  } else if constexpr (FMT == QMOE_MXFP4) {
-    const uint4 q = *(const uint4*)(M.p0 + (size_t)row * (K >> 1) + 16 * (size_t)u);
-    const uint32_t e = M.p1[row * nb32 + u];
-    e2m1_to_h2(q, codes);
-    c0 = e8m0_to_f32(e);
-    c1 = 0.f;
-  } else if constexpr (FMT == QMOE_Q4_K) {
-    const uint4 q = *(const uint4*)(M.p0 + (size_t)row * (K >> 1) + 16 * (size_t)u);
-    const uint4 meta = ((const uint4*)M.p1)[(size_t)row * (K >> 8) + (u >> 3)];
-    const int j = u & 7;
-    const uint64_t lo = (uint64_t)meta.y | ((uint64_t)meta.z << 32);
-    const uint64_t hi = (uint64_t)meta.z | ((uint64_t)meta.w << 32);
-    const float sc = (float)((lo >> (6 * j)) & 63u);
-    const float mn = (float)((hi >> (16 + 6 * j)) & 63u);
-    nibbles_to_h2(q, H2_NEG_1024, codes);
-    c0 = f16_bits_to_f32(meta.x & 0xFFFFu) * sc;
-    c1 = f16_bits_to_f32(meta.x >> 16) * mn;
-  } else {  // Q6_K
-    const uint4 ql = *(const uint4*)(M.p0 + (size_t)row * (K >> 1) + 16 * (size_t)u);
-    const uint2 qh = *(const uint2*)(M.p1 + (size_t)row * (K >> 2) + 8 * (size_t)u);
-    const size_t sb = (size_t)row * (K >> 8) + (u >> 3);
-    const uint32_t sc2 = ((const uint16_t*)(M.p2 + 16 * sb))[u & 7];
-    const float d = f16_bits_to_f32(((const uint16_t*)M.p3)[sb]);
-    q6_to_h2(ql, qh, codes);
-    c0 = d * (float)(int8_t)(sc2 & 0xFFu);
-    c1 = d * (float)(int8_t)(sc2 >> 8);
-  }
-}
+struct Unit {
+  uint4 q, q2;   // codes (q2: second half of a Q8_0 unit)
+  uint4 meta;    // Q4_K superblock meta
+  uint2 qh;      // Q6_K high bits
+  uint32_t s0, s1;
 
-// acc[r] += <unit u of the row, staged activations of row r>
+  QMOE_D void load(const Mat& M, int row, int u, int K) {
+    const size_t nb32 = (size_t)(K >> 5);
+    if constexpr (FMT == QMOE_Q8_0) {
+      const uint4* p = (const uint4*)(M.p0 + (size_t)row * K + 32 * (size_t)u);
+      q = p[0];
+      q2 = p[1];
+      s0 = ((const uint16_t*)M.p1)[row * nb32 + u];
+    } else if constexpr (FMT == QMOE_Q4_0) {
+      q = *(const uint4*)(M.p0 + (size_t)row * (K >> 1) + 16 * (size_t)u);
+      s0 = ((const uint16_t*)M.p1)[row * nb32 + u];
+    } else if constexpr (FMT == QMOE_MXFP4) {
+      q = *(const uint4*)(M.p0 + (size_t)row * (K >> 1) + 16 * (size_t)u);
+      s0 = M.p1[row * nb32 + u];
+    } else if constexpr (FMT == QMOE_Q4_K) {
+      q = *(const uint4*)(M.p0 + (size_t)row * (K >> 1) + 16 * (size_t)u);
+      meta = ((const uint4*)M.p1)[(size_t)row * (K >> 8) + (u >> 3)];
+    } else {
+      q = *(const uint4*)(M.p0 + (size_t)row * (K >> 1) + 16 * (size_t)u);
+      qh = *(const uint2*)(M.p1 + (size_t)row * (K >> 2) + 8 * (size_t)u);
+      const size_t sb = (size_t)row * (K >> 8) + (u >> 3);
+      // the aligned word holding the unit's two sub-block scales (bytes
+      // 2j, 2j+1 of the super-block's 16, j = u & 7; picked at decode)
+      s0 = ((const uint32_t*)(M.p2 + 16 * sb))[(u & 7) >> 1];
+      s1 = ((const uint16_t*)M.p3)[sb];
+    }
+  }
+
+  // unit coefficients (see above)
+  QMOE_D void coefs(int u, float& c0, float& c1) const {
+    if constexpr (FMT == QMOE_Q8_0 || FMT == QMOE_Q4_0) {
+      c0 = f16_bits_to_f32(s0);
+      c1 = 0.f;
+    } else if constexpr (FMT == QMOE_MXFP4) {
+      c0 = e8m0_to_f32(s0);
+      c1 = 0.f;
+    } else if constexpr (FMT == QMOE_Q4_K) {
+      // 6-bit fields of the 96-bit word (y, z, w): sc_j at bit 6j, m_j at
+      // bit 48 + 6j; 32-bit funnel shifts only, so the loaded words are used
+      // in place (no 64-bit register pairs to assemble)
+      // (operands are selected first so that no branch is generated)
+      const uint32_t b = 6u * (uint32_t)(u & 7), bm = b + 16u;
+      const bool lo_b = b < 32u, lo_m = bm < 32u;
+      const uint32_t sc = __builtin_amdgcn_alignbit(lo_b ? meta.z : meta.w, lo_b ? meta.y : meta.z,
+                                                    b & 31u) & 63u;
+      const uint32_t mn = __builtin_amdgcn_alignbit(lo_m ? meta.w : 0u, lo_m ? meta.z : meta.w,
+                                                    bm & 31u) & 63u;
+      c0 = f16_bits_to_f32(meta.x & 0xFFFFu) * (float)sc;
+      c1 = f16_bits_to_f32(meta.x >> 16) * (float)mn;
+    } else {
+      const float d = f16_bits_to_f32(s1);
+      const uint32_t sh = (uint32_t)(u & 1) * 16u;
+      // (the builtin's result type is unsigned: reinterpret before converting)
+      c0 = d * (float)(int)__builtin_amdgcn_sbfe(s0, sh, 8u);
+      c1 = d * (float)(int)__builtin_amdgcn_sbfe(s0, sh + 8u, 8u);
+    }
+  }
+
+  // biased codes in the dot-product pair order (pair_elem_biased)
+  QMOE_D void decode(int u, uint32_t codes[16], float& c0, float& c1) const {
+    if constexpr (FMT == QMOE_Q8_0) bytes_biased(q, q2, codes);
+    else if constexpr (FMT == QMOE_MXFP4) e2m1_natural(q, codes);
+    else if constexpr (FMT == QMOE_Q6_K) q6_biased(q, qh, codes);
+    else nibbles_biased(q, codes);
+    coefs(u, c0, c1);
+  }
+
+  // exact code values (bias removed) in nibble / byte order
+  QMOE_D void decode_exact(int u, uint32_t codes[16], float& c0, float& c1) const {
+    if constexpr (FMT == QMOE_Q8_0) bytes_to_h2(q, q2, codes);
+    else if constexpr (FMT == QMOE_Q4_0) nibbles_to_h2(q, H2_NEG_1032, codes);
+    else if constexpr (FMT == QMOE_MXFP4) e2m1_to_h2(q, codes);
+    else if constexpr (FMT == QMOE_Q4_K) nibbles_to_h2(q, H2_NEG_1024, codes);
+    else q6_to_h2(q, qh, codes);
+    coefs(u, c0, c1);
+  }
+};
+
+// acc[r] += <unit, activations of row r> for r < RC, from the biased codes;
+// bv[r] holds the unit's staged sums (see stage_rows).
 template <int FMT, int RC>
-QMOE_D void unit_mac(const uint32_t codes[16], float c0, float c1, const uint32_t* xs,
-                     const float* sx, int ul, int U, float (&acc)[RC]) {
+QMOE_D void unit_dot(const uint32_t codes[16], float c0, float c1, const uint32_t (&xv)[RC][16],
+                     const float2 (&bv)[RC], float (&acc)[RC]) {
 #pragma unroll
   for (int r = 0; r < RC; ++r) {
-    const uint4* xp = (const uint4*)(xs + ((size_t)r * U + ul) * 16);
-    const uint4 v0 = xp[0], v1 = xp[1], v2 = xp[2], v3 = xp[3];
-    const uint32_t xv[16] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w,
-                             v2.x, v2.y, v2.z, v2.w, v3.x, v3.y, v3.z, v3.w};
     float s0 = 0.f, s1 = 0.f;
     if constexpr (FMT == QMOE_Q6_K) {
 #pragma unroll
-      for (int p = 0; p < 8; ++p) s0 = fdot2(codes[p], xv[p], s0);
+      for (int p = 0; p < 8; ++p) s0 = fdot2(codes[p], xv[r][p], s0);
 #pragma unroll
-      for (int p = 8; p < 16; ++p) s1 = fdot2(codes[p], xv[p], s1);
-      acc[r] += c0 * s0 + c1 * s1;
+      for (int p = 8; p < 16; ++p) s1 = fdot2(codes[p], xv[r][p], s1);
+      acc[r] = fmaf(c1, s1 - bv[r].y, fmaf(c0, s0 - bv[r].x, acc[r]));
     } else {
 #pragma unroll
       for (int p = 0; p < 16; p += 2) {
-        s0 = fdot2(codes[p], xv[p], s0);
-        s1 = fdot2(codes[p + 1], xv[p + 1], s1);
+        s0 = fdot2(codes[p], xv[r][p], s0);
+        s1 = fdot2(codes[p + 1], xv[r][p + 1], s1);
       }
-      acc[r] += c0 * (s0 + s1);
-      if constexpr (FMT == QMOE_Q4_K) acc[r] -= c1 * sx[r * U + ul];
+      acc[r] = fmaf(c0, (s0 + s1) - bv[r].x, acc[r]);
+      if constexpr (FMT == QMOE_Q4_K) acc[r] = fmaf(-c1, bv[r].y, acc[r]);
     }
   }
 }
 
-// Stage activation rows into LDS: for rows r < rc and units ul < U of the
-// chunk starting at value k0, 16 fp16-pair words in the format's pair order,
-// plus the fp32 sum of the unit's 32 values.  `src(r)` gives the row pointer
-// (element 0 of the full-length row) and its dtype is `dtype`.
-template <bool BYTE_PAIRS, class Src>
-QMOE_D void stage_rows(uint32_t* xs, float* sx, int rc, int U, int k0, Src src, int dtype) {
-  for (int idx = threadIdx.x; idx < rc * U; idx += kBlock) {
-    const int r = idx / U, ul = idx - r * U;
-    const void* row = src(r);
-    float v[32];
-    if (dtype == QMOE_F32) {
-      const float4* p = (const float4*)((const float*)row + k0 + 32 * ul);
+// ---------------------------------------------- staged activation rows --
+// Row r of a chunk occupies `tok_stride(U)` bytes of LDS: unit u (16 words)
+// at byte 64u + 16(u/4).  The 16-byte pad after every 4 units puts the 16-byte
+// reads of 8 consecutive lanes (consecutive units) on distinct banks.
+QMOE_HD int tok_stride(int U) { return 64 * U + 16 * ((U + 3) >> 2); }
+QMOE_HD int unit_off(int u) { return 64 * u + 16 * (u >> 2); }
+
+// 32 activation values (fp32 or raw bf16) starting at element 32u of row.
+QMOE_D void load32(const void* row, int dtype, int u, float v[32]) {
+  if (dtype == QMOE_F32) {
+    const float4* p = (const float4*)((const float*)row + 32 * u);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float4 f = p[i];
-        v[4 * i] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
-      }
-    } else {
-      const uint4* p = (const uint4*)((const uint16_t*)row + k0 + 32 * ul);
+    for (int i = 0; i < 8; ++i) {
+      const float4 f = p[i];
+      v[4 * i] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
+    }
+  } else {
+    const uint4* p = (const uint4*)((const uint16_t*)row + 32 * u);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint4 b = p[i];
-        const uint32_t w[4] = {b.x, b.y, b.z, b.w};
+    for (int i = 0; i < 4; ++i) {
+      const uint4 b = p[i];
+      const uint32_t w[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          v[8 * i + 2 * j] = bf16_bits_to_f32(w[j] & 0xFFFFu);
-          v[8 * i + 2 * j + 1] = bf16_bits_to_f32(w[j] >> 16);
-        }
+      for (int j = 0; j < 4; ++j) {
+        v[8 * i + 2 * j] = bf16_bits_to_f32(w[j] & 0xFFFFu);
+        v[8 * i + 2 * j + 1] = bf16_bits_to_f32(w[j] >> 16);
       }
     }
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) s += v[i];
-    sx[idx] = s;
+  }
+}
+
+// Stage rc activation rows for format FMT: per unit, 16 fp16 pair words in
+// the biased-code pair order (odd pairs of the 4/6-bit formats divided by
+// 16) and two fp32 sums that remove the code bias from the unit's dot
+// product.  With S = sum of the staged values and X = sum of the values the
+// codes effectively meet (staged value, times 16 on the divided pairs):
+//   Q4_0: {1024 S + 8 X, 0}          Q4_K: {1024 S, X}  (X meets the min)
+//   Q6_K: {1024 S + 32 X} over elements 0..15 and over 16..31
+//   Q8_0: {1152 S, 0}                MXFP4: {0, 0}
+template <int FMT, class Src>
+QMOE_D void stage_rows(uint8_t* xs, float2* sb, int rc, int U, Src src, int dtype) {
+  const int ts = tok_stride(U);
+  for (int idx = threadIdx.x; idx < rc * U; idx += kBlock) {
+    const int r = idx / U, u = idx - r * U;
+    float v[32];
+    load32(src(r), dtype, u, v);
     uint32_t w[16];
+    float S[2] = {0.f, 0.f}, X[2] = {0.f, 0.f};
 #pragma unroll
     for (int p = 0; p < 16; ++p) {
-      const int e0 = BYTE_PAIRS ? pair_elem_byte(p, 0) : pair_elem_nibble(p, 0);
-      const int e1 = BYTE_PAIRS ? pair_elem_byte(p, 1) : pair_elem_nibble(p, 1);
-      w[p] = pack_h2(v[e0], v[e1]);
+      const bool up4 = pair_up4<FMT>(p);
+      const float sc = up4 ? 0.0625f : 1.f;
+      const float a = f16_bits_to_f32(f32_to_f16_bits(v[pair_elem_biased<FMT>(p, 0)])) * sc;
+      const float b = f16_bits_to_f32(f32_to_f16_bits(v[pair_elem_biased<FMT>(p, 1)])) * sc;
+      w[p] = pack_h2(a, b);
+      const float fa = f16_bits_to_f32(w[p] & 0xFFFFu), fb = f16_bits_to_f32(w[p] >> 16);
+      S[p >> 3] += fa + fb;
+      X[p >> 3] += up4 ? 16.f * (fa + fb) : fa + fb;
     }
-    uint4* dst = (uint4*)(xs + (size_t)idx * 16);
+    float2 out = make_float2(0.f, 0.f);
+    if constexpr (FMT == QMOE_Q4_0) out.x = 1024.f * (S[0] + S[1]) + 8.f * (X[0] + X[1]);
+    if constexpr (FMT == QMOE_Q4_K) out = make_float2(1024.f * (S[0] + S[1]), X[0] + X[1]);
+    if constexpr (FMT == QMOE_Q6_K)
+      out = make_float2(1024.f * S[0] + 32.f * X[0], 1024.f * S[1] + 32.f * X[1]);
+    if constexpr (FMT == QMOE_Q8_0) out.x = 1152.f * (S[0] + S[1]);
+    sb[idx] = out;
+    uint4* dst = (uint4*)(xs + (size_t)r * ts + unit_off(u));
     dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
     dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
     dst[2] = make_uint4(w[8], w[9], w[10], w[11]);
@@ -166,81 +244,319 @@ QMOE_D void stage_rows(uint32_t* xs, float* sx, int rc, int U, int k0, Src src, 
   }
 }
 
-QMOE_D float group_sum_rt(float v, int G) {
-  for (int off = G >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+// ------------------------------------------------ DPP group reduction ---
+template <int CTRL, int ROW_MASK>
+QMOE_D float dpp_move(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF, true));
+}
+
+// Sum over aligned groups of G lanes (G a power of two <= 64); the group's
+// total ends up in its last lane (lane G-1 of the group).
+QMOE_D float group_reduce(float v, int G) {
+  if (G >= 2) v += dpp_move<0x111, 0xF>(v);   // row_shr:1
+  if (G >= 4) v += dpp_move<0x112, 0xF>(v);   // row_shr:2
+  if (G >= 8) v += dpp_move<0x114, 0xF>(v);   // row_shr:4
+  if (G >= 16) v += dpp_move<0x118, 0xF>(v);  // row_shr:8
+  if (G >= 32) v += dpp_move<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  if (G >= 64) v += dpp_move<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
   return v;
 }
 
-// One block computes `rows` (row0 .. row0 + rows_per_block - 1) of NMAT
-// matrices [N, K] against up to RC staged activation rows, for all K chunks.
-// `src(r)` yields activation row r of the chunk; `sink(n, r, acc)` receives the
-// finished dot products (called by one lane per row).
-template <int FMT, int NMAT, int RC, class Src, class Sink>
-QMOE_D void gemv_chunk(const Mat (&mats)[NMAT], int N, int K, int row, int g, int G,
-                       int rc, int kc, int dtype, uint32_t* xs, float* sx, Src src,
-                       Sink sink) {
+// ---------------------------------------------- few rows: fp16 dots -----
+// Rows [rb, re) of NMAT matrices [*, K] against the rc (<= RC) staged rows.
+// sink(row, r, const float* v[NMAT]) is called once per (row, r).
+template <int FMT, int NMAT, int RC, class Sink>
+QMOE_D void valu_pass(const Mat (&mats)[NMAT], int K, int rb, int re, int G, int rc,
+                      const uint8_t* xs, const float2* sb, Sink sink) {
+  constexpr int D = NMAT == 2 ? 3 : 4;  // units in flight per lane
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = 64 / G, g = lane & (G - 1), slot = lane / G;
+  const int U = K >> 5, UPL = U / G, ts = tok_stride(U);
+  const int first = rb + wave * sub, step = kWaves * sub;
+  const int n_rg = first < re ? (re - first + step - 1) / step : 0;
+  const int nflat = n_rg * UPL;
+
+  if (nflat == 0) return;  // wave-uniform
+
+  // Every load is unconditional: positions past the wave's last (row group,
+  // unit) re-read the tile's last row, so no load sits behind a branch and
+  // each slot's data is consumed in the registers it was loaded into.
+  Unit<FMT> buf[D][NMAT];
+  int irg = 0, it = 0;  // next (row group, unit) to load
+  auto issue = [&](Unit<FMT> (&w)[NMAT]) {
+    const int row = min(first + irg * step + slot, re - 1);
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) w[m].load(mats[m], row, g + it * G, K);
+    if (++it == UPL) { it = 0; ++irg; }
+  };
+  auto compute = [&](Unit<FMT> (&w)[NMAT], int u, float (&acc)[NMAT][RC]) {
+    uint32_t xv[RC][16];
+    float2 bv[RC];
+#pragma unroll
+    for (int r = 0; r < RC; ++r) {
+      if (r < rc) {
+        const uint4* xp = (const uint4*)(xs + (size_t)r * ts + unit_off(u));
+        const uint4 v0 = xp[0], v1 = xp[1], v2 = xp[2], v3 = xp[3];
+        xv[r][0] = v0.x; xv[r][1] = v0.y; xv[r][2] = v0.z; xv[r][3] = v0.w;
+        xv[r][4] = v1.x; xv[r][5] = v1.y; xv[r][6] = v1.z; xv[r][7] = v1.w;
+        xv[r][8] = v2.x; xv[r][9] = v2.y; xv[r][10] = v2.z; xv[r][11] = v2.w;
+        xv[r][12] = v3.x; xv[r][13] = v3.y; xv[r][14] = v3.z; xv[r][15] = v3.w;
+        bv[r] = FMT == QMOE_MXFP4 ? make_float2(0.f, 0.f) : sb[r * U + u];
+      } else {
+#pragma unroll
+        for (int p = 0; p < 16; ++p) xv[r][p] = 0u;
+        bv[r] = make_float2(0.f, 0.f);
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) {
+      uint32_t codes[16];
+      float c0, c1;
+      w[m].decode(u, codes, c0, c1);
+      unit_dot<FMT, RC>(codes, c0, c1, xv, bv, acc[m]);
+    }
+  };
+
+  // The slots are filled in the order the loop consumes them (the barrier
+  // keeps the scheduler from interleaving them), so before each compute the
+  // wait leaves the younger slots' loads in flight.
+#pragma unroll
+  for (int i = 0; i < D; ++i) {
+    issue(buf[i]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   float acc[NMAT][RC];
 #pragma unroll
   for (int m = 0; m < NMAT; ++m)
 #pragma unroll
     for (int r = 0; r < RC; ++r) acc[m][r] = 0.f;
-
-  for (int k0 = 0; k0 < K; k0 += kc) {
-    const int kcur = min(kc, K - k0);
-    const int U = kcur >> 5;
-    __syncthreads();  // previous users of xs are done
-    stage_rows<byte_order(FMT)>(xs, sx, rc, U, k0, src, dtype);
-    __syncthreads();
-    if (row < N) {
-      const int ub = k0 >> 5;
-      for (int ul = g; ul < U; ul += G) {
+  int crg = 0, ct = 0;  // (row group, unit) being computed
+  // nflat rounded up to a multiple of D: the extra positions are computed on
+  // re-read data and never stored (their row group is past the last)
+  for (int f0 = 0; f0 < nflat; f0 += D) {
 #pragma unroll
-        for (int m = 0; m < NMAT; ++m) {
-          uint32_t codes[16];
-          float c0, c1;
-          load_unit<FMT>(mats[m], row, ub + ul, K, codes, c0, c1);
-          unit_mac<FMT, RC>(codes, c0, c1, xs, sx, ul, U, acc[m]);
+    for (int i = 0; i < D; ++i) {
+      compute(buf[i], g + ct * G, acc);
+      issue(buf[i]);
+      if (++ct == UPL) {  // wave-uniform
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+          for (int r = 0; r < RC; ++r) acc[m][r] = group_reduce(acc[m][r], G);
+        const int row = first + crg * step + slot;
+        if (crg < n_rg && row < re && g == G - 1) {
+#pragma unroll
+          for (int r = 0; r < RC; ++r) {
+            if (r < rc) {
+              float v[NMAT];
+#pragma unroll
+              for (int m = 0; m < NMAT; ++m) v[m] = acc[m][r];
+              sink(row, r, v);
+            }
+          }
         }
-      }
-    }
-  }
 #pragma unroll
-  for (int m = 0; m < NMAT; ++m)
+        for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-    for (int r = 0; r < RC; ++r) acc[m][r] = group_sum_rt(acc[m][r], G);
-  if (row < N && g == 0) {
-#pragma unroll
-    for (int r = 0; r < RC; ++r) {
-      if (r < rc) {
-        float a[NMAT];
-#pragma unroll
-        for (int m = 0; m < NMAT; ++m) a[m] = acc[m][r];
-        sink(row, r, a);
+          for (int r = 0; r < RC; ++r) acc[m][r] = 0.f;
+        ct = 0;
+        ++crg;
       }
     }
   }
 }
 
-// Run gemv_chunk for `rows_total` activation rows in chunks of at most rcl,
-// picking the register-blocking RC (1, 2, 4, 8, 16) per chunk.
+// Stage up to RC rows at a time and stream the tile against them.
+template <int FMT, int NMAT, int RC, class SrcOf, class SinkOf>
+QMOE_D void valu_rows(const Mat (&mats)[NMAT], int K, int rb, int re, int G, int rows_total,
+                      int dtype, uint8_t* lds, SrcOf src_of, SinkOf sink_of) {
+  const int U = K >> 5;
+  uint8_t* xs = lds;
+  float2* sb = (float2*)(lds + (size_t)RC * tok_stride(U));
+  for (int c0 = 0; c0 < rows_total; c0 += RC) {
+    const int rc = min(RC, rows_total - c0);
+    __syncthreads();
+    stage_rows<FMT>(xs, sb, rc, U, [&](int r) { return src_of(c0 + r); }, dtype);
+    __syncthreads();
+    valu_pass<FMT, NMAT, RC>(mats, K, rb, re, G, rc, xs, sb,
+                             [&](int n, int r, const float* a) { sink_of(n, c0 + r, a); });
+  }
+}
+
+// ------------------------------------------- many rows: matrix cores ----
+// Weight rows [cb, ce) of NMAT matrices [N, K] (the output columns) against
+// rows_total activation rows, in 16 x 16 output tiles on the matrix cores
+// (v_mfma_f32_16x16x32_f16, fp32 accumulation).  The 4 waves of the block
+// split K: wave w takes the 128-value quads w, w + 4, ... and the four
+// partial tiles are added in LDS in wave order.  Lane (n = lane % 16,
+// g = lane / 16) holds unit 4Q + g of weight row c + n and the same 32 values
+// of activation row n: the unit's exact fp16 codes (as on the dot-product
+// path) scaled in fp16, and the activations rounded to fp16, both listed in
+// the format's pair order, so the two operands agree on every K slot.  Loads
+// run one quad ahead of the matrix-core work.
+
+// 32 raw activation values (fp32: 8 x 16 B; bf16: the first 4 x 16 B),
+// converted only where they are used so the loads stay in flight.
+struct XRaw {
+  uint4 r[8];
+};
+
+QMOE_D void xraw_load(const void* row, int dtype, int u, XRaw& x) {
+  if (dtype == QMOE_F32) {
+    const uint4* p = (const uint4*)((const float*)row + 32 * u);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x.r[i] = p[i];
+  } else {
+    const uint4* p = (const uint4*)((const uint16_t*)row + 32 * u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x.r[i] = p[i];
+  }
+}
+
+QMOE_D uint32_t word_of(const uint4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// fp16 pairs of the 32 values in the pair order of format FMT
+template <int FMT>
+QMOE_D void xraw_pairs(const XRaw& x, int dtype, uint32_t out[16]) {
+  if (dtype == QMOE_F32) {
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+      const int e0 = byte_order(FMT) ? pair_elem_byte(p, 0) : pair_elem_nibble(p, 0);
+      const int e1 = byte_order(FMT) ? pair_elem_byte(p, 1) : pair_elem_nibble(p, 1);
+      out[p] = pack_f16(__builtin_bit_cast(float, word_of(x.r[e0 >> 2], e0 & 3)),
+                        __builtin_bit_cast(float, word_of(x.r[e1 >> 2], e1 & 3)));
+    }
+  } else {
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+      const int e0 = byte_order(FMT) ? pair_elem_byte(p, 0) : pair_elem_nibble(p, 0);
+      const int e1 = byte_order(FMT) ? pair_elem_byte(p, 1) : pair_elem_nibble(p, 1);
+      const uint32_t w0 = word_of(x.r[e0 >> 3], (e0 >> 1) & 3);
+      const uint32_t w1 = word_of(x.r[e1 >> 3], (e1 >> 1) & 3);
+      out[p] = pack_f16(bf16_bits_to_f32((e0 & 1) ? w0 >> 16 : w0 & 0xFFFFu),
+                        bf16_bits_to_f32((e1 & 1) ? w1 >> 16 : w1 & 0xFFFFu));
+    }
+  }
+}
+
+// Unit values in fp16: codes times the unit coefficients (minus the Q4_K
+// offset), one packed fp16 operation per pair.
+template <int FMT>
+QMOE_D void scale_codes(const uint32_t codes[16], float c0, float c1, uint32_t out[16]) {
+  if constexpr (FMT == QMOE_Q4_K) {
+    const h2_t a = __builtin_bit_cast(h2_t, pack_f16(c0, c0));
+    const h2_t b = __builtin_bit_cast(h2_t, pack_f16(-c1, -c1));
+#pragma unroll
+    for (int p = 0; p < 16; ++p)
+      out[p] = __builtin_bit_cast(uint32_t,
+                                  __builtin_elementwise_fma(__builtin_bit_cast(h2_t, codes[p]), a, b));
+  } else if constexpr (FMT == QMOE_Q6_K) {
+    const uint32_t a = pack_f16(c0, c0), b = pack_f16(c1, c1);
+#pragma unroll
+    for (int p = 0; p < 16; ++p) out[p] = pk_mul_h2(codes[p], p < 8 ? a : b);
+  } else {
+    const uint32_t a = pack_f16(c0, c0);
+#pragma unroll
+    for (int p = 0; p < 16; ++p) out[p] = pk_mul_h2(codes[p], a);
+  }
+}
+
+QMOE_HD size_t mfma_red_bytes(int nmat) { return (size_t)kWaves * nmat * 4 * 64 * sizeof(float); }
+
 template <int FMT, int NMAT, class SrcOf, class SinkOf>
-QMOE_D void gemv_rows(const Mat (&mats)[NMAT], int N, int K, int row, int g, int G,
-                      int rows_total, int rcl, int kc, int dtype, uint32_t* xs, float* sx,
-                      SrcOf src_of, SinkOf sink_of) {
-  for (int c0 = 0; c0 < rows_total; c0 += rcl) {
-    const int rc = min(rcl, rows_total - c0);
-    auto src = [&](int r) { return src_of(c0 + r); };
-    auto sink = [&](int n, int r, const float* a) { sink_of(n, c0 + r, a); };
-    if (rc == 1)
-      gemv_chunk<FMT, NMAT, 1>(mats, N, K, row, g, G, rc, kc, dtype, xs, sx, src, sink);
-    else if (rc == 2)
-      gemv_chunk<FMT, NMAT, 2>(mats, N, K, row, g, G, rc, kc, dtype, xs, sx, src, sink);
-    else if (rc <= 4)
-      gemv_chunk<FMT, NMAT, 4>(mats, N, K, row, g, G, rc, kc, dtype, xs, sx, src, sink);
-    else if (rc <= 8)
-      gemv_chunk<FMT, NMAT, 8>(mats, N, K, row, g, G, rc, kc, dtype, xs, sx, src, sink);
-    else
-      gemv_chunk<FMT, NMAT, 16>(mats, N, K, row, g, G, rc, kc, dtype, xs, sx, src, sink);
+QMOE_D void mfma_cols(const Mat (&mats)[NMAT], int K, int cb, int ce, int rows_total, int dtype,
+                      uint8_t* lds, SrcOf src_of, SinkOf sink_of) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int U = K >> 5, nquad = (U + 3) >> 2;
+  float* red = (float*)lds;  // [kWaves][NMAT][4][64]
+  __syncthreads();           // earlier readers of the LDS are done
+  for (int c = cb; c < ce; c += 16) {
+    const int col = c + n;
+    const bool cvalid = col < ce;
+    for (int c0 = 0; c0 < rows_total; c0 += 16) {
+      const int ar = c0 + n;
+      const bool rvalid = ar < rows_total;
+      const void* xrow = src_of(rvalid ? ar : 0);
+      f32x4_t acc[NMAT];
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      // One load buffer per operand: each is decoded into operand registers
+      // and at once refilled with the wave's next quad, so the matrix-core
+      // work runs while those loads are in flight.
+      Unit<FMT> w[NMAT];
+      XRaw x;
+      auto fetch_x = [&](int Q) {
+        const int u = 4 * Q + g;
+        if (u < U && rvalid) {
+          xraw_load(xrow, dtype, u, x);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) x.r[i] = make_uint4(0u, 0u, 0u, 0u);
+        }
+      };
+      if (wave < nquad) {
+        fetch_x(wave);
+        if (4 * wave + g < U && cvalid) {
+#pragma unroll
+          for (int m = 0; m < NMAT; ++m) w[m].load(mats[m], col, 4 * wave + g, K);
+        }
+      }
+      for (int Q = wave; Q < nquad; Q += kWaves) {
+        const int u = 4 * Q + g, un = u + 4 * kWaves;
+        const bool more = Q + kWaves < nquad;
+        uint32_t xv[16];
+        xraw_pairs<FMT>(x, dtype, xv);
+        if (more) fetch_x(Q + kWaves);
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) {
+          uint32_t wv[16];
+          if (u < U && cvalid) {
+            uint32_t codes[16];
+            float s0, s1;
+            w[m].decode_exact(u, codes, s0, s1);
+            scale_codes<FMT>(codes, s0, s1, wv);
+          } else {
+#pragma unroll
+            for (int p = 0; p < 16; ++p) wv[p] = 0u;
+          }
+          if (more && un < U && cvalid) w[m].load(mats[m], col, un, K);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint4 a = make_uint4(xv[4 * q], xv[4 * q + 1], xv[4 * q + 2], xv[4 * q + 3]);
+            const uint4 b = make_uint4(wv[4 * q], wv[4 * q + 1], wv[4 * q + 2], wv[4 * q + 3]);
+            acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                            __builtin_bit_cast(f16x8_t, b),
+                                                            acc[m], 0, 0, 0);
+          }
+        }
+      }
+      // lane holds activation rows c0 + 4g + j (j < 4) of weight row col
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) red[((wave * NMAT + m) * 4 + j) * 64 + lane] = acc[m][j];
+      __syncthreads();
+      {
+        const int j = wave;  // wave j finishes row 4g + j of every lane's tile
+        const int r = c0 + 4 * g + j;
+        if (cvalid && r < rows_total) {
+          float v[NMAT];
+#pragma unroll
+          for (int m = 0; m < NMAT; ++m) {
+            float sum = red[((0 * NMAT + m) * 4 + j) * 64 + lane];
+#pragma unroll
+            for (int w = 1; w < kWaves; ++w) sum += red[((w * NMAT + m) * 4 + j) * 64 + lane];
+            v[m] = sum;
+          }
+          sink_of(col, r, v);
+        }
+      }
+      __syncthreads();
+    }
   }
 }
 
@@ -251,24 +567,24 @@ struct GemvParams {
   const void* x;
   int x_dtype, R;
   float* y;
-  int G, rcl, kc;
+  int G, tile_rows;
 };
 
-template <int FMT>
+template <int FMT, int RC, bool MFMA>
 __global__ __launch_bounds__(kBlock) void qgemv_kernel(GemvParams P) {
-  extern __shared__ __align__(16) uint32_t smem[];
-  const int G = P.G, sub = 64 / G;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int row = (blockIdx.x * kWaves + wave) * sub + lane / G;
-  const int g = lane & (G - 1);
-  uint32_t* xs = smem;
-  float* sx = (float*)(smem + (size_t)P.rcl * P.kc / 2);
-  const Mat mats[1] = {mat_of(P.W, FMT, P.N, P.K)};
-  const int esz = P.x_dtype == QMOE_F32 ? 4 : 2;
-  gemv_rows<FMT, 1>(
-      mats, P.N, P.K, row, g, G, P.R, P.rcl, P.kc, P.x_dtype, xs, sx,
-      [&](int r) { return (const void*)((const char*)P.x + (size_t)r * P.K * esz); },
-      [&](int n, int r, const float* a) { P.y[(size_t)r * P.N + n] = a[0]; });
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int N = P.N, K = P.K, dtype = P.x_dtype;
+  const char* xb = (const char*)P.x;
+  float* y = P.y;
+  const Mat mats[1] = {mat_of(P.W, FMT, N, K)};
+  const int rb = blockIdx.x * P.tile_rows, re = min(N, rb + P.tile_rows);
+  const size_t xrow_bytes = (size_t)K * (dtype == QMOE_F32 ? 4 : 2);
+  auto src = [=](int r) { return (const void*)(xb + (size_t)r * xrow_bytes); };
+  auto sink = [=](int n, int r, const float* a) { y[(size_t)r * N + n] = a[0]; };
+  if (MFMA)
+    mfma_cols<FMT, 1>(mats, K, rb, re, P.R, dtype, smem, src, sink);
+  else
+    valu_rows<FMT, 1, RC>(mats, K, rb, re, P.G, P.R, dtype, smem, src, sink);
 }
 
 // ------------------------------------------------------- routed FFN -----
@@ -281,87 +597,145 @@ struct FfnParams {
   const int32_t* perm;
   float* h;  // [T*k, F] workspace (SwiGLU output, permuted rows)
   float* o;  // [T*k, H]
-  int ntiles, G, rcl, kc;
+  int ntiles, G, tile_rows;
+  int m_max;       // experts with more rows use the matrix cores
+  int ntiles_big;  // blocks (column tiles) per such expert
 };
 
-// The expert whose first permuted position is `slot`, or -1.  Positions of
-// expert e are offsets[e] .. offsets[e+1]-1; ids outside [0, E) never got a
-// position, so they are never visited ([P2] bug items 1 and 3).
-QMOE_D int expert_at(const int32_t* offsets, int E, int slot) {
-  if (slot >= offsets[E]) return -1;
-  int lo = 0, hi = E;  // invariant: offsets[lo] <= slot
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (offsets[mid] <= slot) lo = mid; else hi = mid;
+// The tier holding expert e, assembled field by field with constant indices
+// only: any runtime index or struct copy out of the by-value kernel argument
+// would make the compiler spill the whole argument block to scratch.
+QMOE_D bool tier_of(const qmoe_tier (&tiers)[QMOE_MAX_TIERS], int n_tiers, int e,
+                    qmoe_tier& out) {
+  bool found = false;
+  int32_t eb = 0, ee = 0, fgu = 0, fd = 0;
+  const void *g = nullptr, *u = nullptr, *d = nullptr;
+#pragma unroll
+  for (int i = 0; i < QMOE_MAX_TIERS; ++i) {
+    const bool hit = !found && i < n_tiers && e >= tiers[i].e_begin && e < tiers[i].e_end;
+    if (hit) {
+      eb = tiers[i].e_begin; ee = tiers[i].e_end;
+      fgu = tiers[i].fmt_gate_up; fd = tiers[i].fmt_down;
+      g = tiers[i].gate; u = tiers[i].up; d = tiers[i].down;
+      found = true;
+    }
   }
-  return offsets[lo] == slot ? lo : -1;
-}
-
-QMOE_D const qmoe_tier* tier_of(const FfnParams& P, int e) {
-  for (int i = 0; i < P.n_tiers; ++i)
-    if (e >= P.tiers[i].e_begin && e < P.tiers[i].e_end) return &P.tiers[i];
-  return nullptr;
+  out.e_begin = eb; out.e_end = ee; out.fmt_gate_up = fgu; out.fmt_down = fd;
+  out.gate = g; out.up = u; out.down = d;
+  return found;
 }
 
 QMOE_D float silu_mul(float g, float u) { return g / (1.f + expf(-g)) * u; }
 
-template <int FMT>
-QMOE_D void ffn_gate_up_body(const FfnParams& P, const qmoe_tier* t, int e, int pos0, int m,
-                             int tile, uint32_t* xs, float* sx) {
-  const int G = P.G, sub = 64 / G;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int row = (tile * kWaves + wave) * sub + lane / G;
-  const int g = lane & (G - 1);
-  const size_t stride = layout_of(FMT, P.F, P.H).total;
-  const size_t eo = (size_t)(e - t->e_begin) * stride;
-  const Mat mats[2] = {mat_of((const uint8_t*)t->gate + eo, FMT, P.F, P.H),
-                       mat_of((const uint8_t*)t->up + eo, FMT, P.F, P.H)};
-  const int esz = P.x_dtype == QMOE_F32 ? 4 : 2;
-  gemv_rows<FMT, 2>(
-      mats, P.F, P.H, row, g, G, m, P.rcl, P.kc, P.x_dtype, xs, sx,
-      [&](int r) {
-        const int tok = P.perm[pos0 + r] / P.k;
-        return (const void*)((const char*)P.x + (size_t)tok * P.H * esz);
-      },
-      [&](int n, int r, const float* a) {
-        P.h[(size_t)(pos0 + r) * P.F + n] = silu_mul(a[0], a[1]);
-      });
+// Block schedule.  Experts with more than m_max rows ("big") come first with
+// ntiles_big blocks each, then the experts with 1..m_max rows with ntiles
+// blocks each, both groups in id order.  Returns the expert of block b (-1
+// past the end) and sets its tile index and group.  offs (E+1 entries) and
+// red (2 * kWaves + 2 ints) are in LDS.  Block-wide; every thread gets the
+// result.  Experts never routed to have no rows and are never scheduled, nor
+// are ids outside [0, E) ([P2] bug items 1 and 3).
+QMOE_D int scheduled_expert(const int* offs, int E, int m_max, int b, int ntiles,
+                            int ntiles_big, int* red, int& tile, bool& big) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int per = (E + kBlock - 1) / kBlock;
+  const int lo = min(E, tid * per), hi = min(E, lo + per);
+  int nb = 0, ns = 0;
+  for (int e = lo; e < hi; ++e) {
+    const int m = offs[e + 1] - offs[e];
+    nb += m > m_max;
+    ns += m > 0 && m <= m_max;
+  }
+  int sb = nb, ss = ns;  // inclusive scans within the wave
+  for (int off = 1; off < 64; off <<= 1) {
+    const int ob = __shfl_up(sb, off, 64), os = __shfl_up(ss, off, 64);
+    if (lane >= off) { sb += ob; ss += os; }
+  }
+  if (lane == 63) { red[wave] = sb; red[kWaves + wave] = ss; }
+  if (tid == 0) red[2 * kWaves] = -1;
+  __syncthreads();
+  int bb = 0, bs = 0, tb = 0, ts = 0;
+  for (int w = 0; w < kWaves; ++w) {
+    if (w < wave) { bb += red[w]; bs += red[kWaves + w]; }
+    tb += red[w];
+    ts += red[kWaves + w];
+  }
+  const int xb = bb + sb - nb, xs = bs + ss - ns;  // exclusive prefixes of this slice
+  const long long big_blocks = (long long)tb * ntiles_big;
+  big = b < big_blocks;
+  const int rel = big ? b : (int)(b - big_blocks);
+  const int per_expert = big ? ntiles_big : ntiles;
+  const int want = rel / per_expert;
+  tile = rel - want * per_expert;
+  const int first = big ? xb : xs, count = big ? nb : ns;
+  if ((big || want < ts) && want >= first && want < first + count) {
+    int c = first;
+    for (int e = lo; e < hi; ++e) {
+      const int m = offs[e + 1] - offs[e];
+      if (big ? m > m_max : (m > 0 && m <= m_max)) {
+        if (c == want) { red[2 * kWaves] = e; break; }
+        ++c;
+      }
+    }
+  }
+  __syncthreads();
+  return red[2 * kWaves];
 }
 
-template <int FMT>
-QMOE_D void ffn_down_body(const FfnParams& P, const qmoe_tier* t, int e, int pos0, int m,
-                          int tile, uint32_t* xs, float* sx) {
-  const int G = P.G, sub = 64 / G;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int row = (tile * kWaves + wave) * sub + lane / G;
-  const int g = lane & (G - 1);
-  const size_t stride = layout_of(FMT, P.H, P.F).total;
-  const Mat mats[1] = {mat_of((const uint8_t*)t->down + (size_t)(e - t->e_begin) * stride,
-                              FMT, P.H, P.F)};
-  gemv_rows<FMT, 1>(
-      mats, P.H, P.F, row, g, G, m, P.rcl, P.kc, QMOE_F32, xs, sx,
-      [&](int r) { return (const void*)(P.h + (size_t)(pos0 + r) * P.F); },
-      [&](int n, int r, const float* a) { P.o[(size_t)(pos0 + r) * P.H + n] = a[0]; });
-}
-
-// PHASE 0: gate/up + SwiGLU -> h;  PHASE 1: down -> o.
-template <int PHASE>
+// PHASE 0: gate/up + SwiGLU -> h;  PHASE 1: down -> o.  MFMA: whether
+// experts with more than m_max rows can occur (the matrix-core branch costs
+// registers, so launches that cannot use it leave it out).
+template <int PHASE, int RC, bool MFMA>
 __global__ __launch_bounds__(kBlock) void ffn_decode_kernel(FfnParams P) {
-  extern __shared__ __align__(16) uint32_t smem[];
-  const int slot = blockIdx.x / P.ntiles, tile = blockIdx.x - slot * P.ntiles;
-  const int e = expert_at(P.offsets, P.E, slot);
+  extern __shared__ __align__(16) uint8_t smem[];
+  // scalars used below, read once from the argument block
+  const int E = P.E, H = P.H, F = P.F, kk = P.k, dtype = P.x_dtype, m_max = P.m_max;
+  const int ntiles = P.ntiles, G = P.G, tile_rows = P.tile_rows;
+  const int32_t* perm = P.perm;
+  const char* xb = (const char*)P.x;
+  float* hbuf = P.h;
+  float* obuf = P.o;
+  int* offs = (int*)smem;
+  int* red = offs + E + 1;
+  for (int i = threadIdx.x; i <= E; i += kBlock) offs[i] = P.offsets[i];
+  __syncthreads();
+  int tile = 0;
+  bool big = false;
+  const int e = scheduled_expert(offs, E, m_max, blockIdx.x, ntiles, P.ntiles_big, red, tile, big);
   if (e < 0) return;
-  const qmoe_tier* t = tier_of(P, e);
-  if (!t) return;
-  const int m = P.offsets[e + 1] - slot;
-  uint32_t* xs = smem;
-  float* sx = (float*)(smem + (size_t)P.rcl * P.kc / 2);
-  const int fmt = PHASE == 0 ? t->fmt_gate_up : t->fmt_down;
-#define QMOE_FFN_CASE(F)                                                   \
-  case F:                                                                  \
-    if (PHASE == 0) ffn_gate_up_body<F>(P, t, e, slot, m, tile, xs, sx);   \
-    else ffn_down_body<F>(P, t, e, slot, m, tile, xs, sx);                 \
-    break;
+  const int pos0 = offs[e], m = offs[e + 1] - offs[e];
+  qmoe_tier t;
+  if (!tier_of(P.tiers, P.n_tiers, e, t)) return;
+  const int fmt = PHASE == 0 ? t.fmt_gate_up : t.fmt_down;
+  const int N = PHASE == 0 ? F : H, K = PHASE == 0 ? H : F;
+  // few-row experts: weight rows [rb, re) of a row tile; many-row experts:
+  // a 16-aligned column slice, N split over ntiles_big blocks
+  const int cpt = ((N + P.ntiles_big - 1) / P.ntiles_big + 15) / 16 * 16;
+  const int rb = big ? tile * cpt : tile * tile_rows;
+  const int re = min(N, rb + (big ? cpt : tile_rows));
+  if (rb >= re) return;
+  const size_t xrow_bytes = (size_t)H * (dtype == QMOE_F32 ? 4 : 2);
+  auto x_row = [=](int rr) {
+    return (const void*)(xb + (size_t)(perm[pos0 + rr] / kk) * xrow_bytes);
+  };
+  auto h_out = [=](int n, int rr, const float* a) {
+    hbuf[(size_t)(pos0 + rr) * F + n] = silu_mul(a[0], a[1]);
+  };
+  auto h_row = [=](int rr) { return (const void*)(hbuf + (size_t)(pos0 + rr) * F); };
+  auto o_out = [=](int n, int rr, const float* a) { obuf[(size_t)(pos0 + rr) * H + n] = a[0]; };
+#define QMOE_FFN_CASE(FM)                                                                  \
+  case FM: {                                                                               \
+    const size_t eo = (size_t)(e - t.e_begin) * layout_of(FM, N, K).total;                  \
+    if (PHASE == 0) {                                                                      \
+      const Mat mats[2] = {mat_of((const uint8_t*)t.gate + eo, FM, N, K),                  \
+                           mat_of((const uint8_t*)t.up + eo, FM, N, K)};                   \
+      if (MFMA && big) mfma_cols<FM, 2>(mats, K, rb, re, m, dtype, smem, x_row, h_out);             \
+      else valu_rows<FM, 2, RC>(mats, K, rb, re, G, m, dtype, smem, x_row, h_out);         \
+    } else {                                                                               \
+      const Mat mats[1] = {mat_of((const uint8_t*)t.down + eo, FM, N, K)};                 \
+      if (MFMA && big) mfma_cols<FM, 1>(mats, K, rb, re, m, QMOE_F32, smem, h_row, o_out);         \
+      else valu_rows<FM, 1, RC>(mats, K, rb, re, G, m, QMOE_F32, smem, h_row, o_out);      \
+    }                                                                                      \
+  } break;
   switch (fmt) {
     QMOE_FFN_CASE(QMOE_Q8_0)
     QMOE_FFN_CASE(QMOE_Q4_0)
@@ -374,59 +748,99 @@ __global__ __launch_bounds__(kBlock) void ffn_decode_kernel(FfnParams P) {
 }
 
 // ------------------------------------------------------ host helpers ----
-// Lanes per weight row: the largest power of two <= 64 dividing K/32.
+// Lanes per weight row: the largest power of two <= 64 dividing the unit
+// count K/32 that still leaves every lane >= 4 units.
 static int lanes_per_row(int K) {
   const int units = K / 32;
   int G = 1;
-  while (G < 64 && units % (2 * G) == 0) G *= 2;
+  while (G < 64 && units % (2 * G) == 0 && units / (2 * G) >= 4) G *= 2;
   return G;
 }
 
-// Activation rows per chunk and values per K-chunk for a given row count.
-static void chunking(int rows, int K, int G, int& rcl, int& kc) {
-  rcl = 1;
-  while (rcl < 16 && rcl < rows) rcl *= 2;
-  kc = K;
-  if ((size_t)rcl * K > (size_t)kXCap) {
-    kc = kXCap / rcl;
-    const int step = 32 * G;
-    kc = kc >= step ? kc / step * step : kc / 32 * 32;
-  }
+static size_t stage_bytes(int RC, int K) {
+  const int U = K / 32;
+  return (size_t)RC * tok_stride(U) + (size_t)RC * U * sizeof(float2);
 }
 
-static size_t smem_bytes(int rcl, int kc) {
-  return (size_t)rcl * kc * 2 + (size_t)rcl * (kc / 32) * 4;
+// Rows per register pass: 1, 2 or 4 (enough for `rows`), halved until the
+// staged rows fit `budget` bytes of LDS.  0 if even one row does not fit.
+static int pick_rc(int rows, int K, size_t budget = kLdsCap) {
+  int rc = rows <= 1 ? 1 : rows <= 2 ? 2 : 4;
+  while (rc > 1 && stage_bytes(rc, K) > budget) rc >>= 1;
+  return stage_bytes(rc, K) <= (size_t)kLdsCap ? rc : 0;
 }
 
-static bool bad_fmt(int fmt) { return fmt < QMOE_Q8_0 || fmt > QMOE_Q6_K; }
+// Rows per block for N rows when `work_items` independent matrices run in
+// the same launch: about eight blocks per compute unit overall, so that every
+// CU keeps enough weight loads in flight to cover HBM latency.  A multiple of
+// a wave pass and of the 16-row matrix-core blocks.
+static int pick_tile_rows(int N, int G, int work_items) {
+  int group = kWaves * (64 / G);
+  if (group < 16) group = 16;
+  int cus = cu_count();
+  if (cus <= 0) cus = 256;
+  const long long want = 8LL * cus;
+  long long tiles = (want + work_items - 1) / work_items;
+  const long long max_tiles = (N + group - 1) / group;
+  if (tiles > max_tiles) tiles = max_tiles;
+  if (tiles < 1) tiles = 1;
+  const int rows = (int)((N + tiles - 1) / tiles);
+  return (rows + group - 1) / group * group;
+}
+
+template <int FMT>
+static int qgemv_dispatch(const GemvParams& P, int RC, dim3 grid, size_t lds, hipStream_t s) {
+  if (P.R > RC) return QMOE_LAUNCH("qgemv", (qgemv_kernel<FMT, 4, true>), grid, kBlock, lds, s, P);
+  if (RC == 1) return QMOE_LAUNCH("qgemv", (qgemv_kernel<FMT, 1, false>), grid, kBlock, lds, s, P);
+  if (RC == 2) return QMOE_LAUNCH("qgemv", (qgemv_kernel<FMT, 2, false>), grid, kBlock, lds, s, P);
+  return QMOE_LAUNCH("qgemv", (qgemv_kernel<FMT, 4, false>), grid, kBlock, lds, s, P);
+}
 
 static int qgemv_launch(int FMT, const void* W, int N, int K, const void* x, int x_dtype,
                         int R, float* y, void* stream) {
   if (!W || !x || !y) return fail(QMOE_ERR_INVALID_ARG, "qgemv: null pointer");
-  if (N < 0 || K <= 0 || R < 0 || K % block_of(FMT) || K > 65536)
+  if (N < 0 || K <= 0 || R < 0 || K % block_of(FMT))
     return fail(QMOE_ERR_INVALID_ARG, "qgemv: bad sizes N=%d K=%d R=%d", N, K, R);
   if (x_dtype != QMOE_F32 && x_dtype != QMOE_BF16)
     return fail(QMOE_ERR_UNSUPPORTED, "qgemv: unknown x_dtype %d", x_dtype);
   if (!QMOE_ALIGNED(W, 256) || !QMOE_ALIGNED(x, 16) || !QMOE_ALIGNED(y, 4))
     return fail(QMOE_ERR_INVALID_ARG, "qgemv: misaligned pointer");
+  const int RC = pick_rc(R, K);
+  if (!RC) return fail(QMOE_ERR_UNSUPPORTED, "qgemv: K=%d too large (max 28672)", K);
   if (N == 0 || R == 0) return QMOE_OK;
-  GemvParams P{W, N, K, x, x_dtype, R, y, 0, 0, 0};
-  P.G = lanes_per_row(K);
-  chunking(R, K, P.G, P.rcl, P.kc);
-  const int rows_per_block = kWaves * (64 / P.G);
-  const dim3 grid((N + rows_per_block - 1) / rows_per_block);
-  const size_t lds = smem_bytes(P.rcl, P.kc);
+  GemvParams P{W, N, K, x, x_dtype, R, y, lanes_per_row(K), 0};
+  P.tile_rows = pick_tile_rows(N, P.G, 1);
+  const dim3 grid((N + P.tile_rows - 1) / P.tile_rows);
+  const size_t lds = R > RC ? mfma_red_bytes(1) : stage_bytes(RC, K);
   hipStream_t s = (hipStream_t)stream;
   switch (FMT) {
-    case QMOE_Q8_0: return QMOE_LAUNCH("qgemv", qgemv_kernel<QMOE_Q8_0>, grid, kBlock, lds, s, P);
-    case QMOE_Q4_0: return QMOE_LAUNCH("qgemv", qgemv_kernel<QMOE_Q4_0>, grid, kBlock, lds, s, P);
-    case QMOE_MXFP4: return QMOE_LAUNCH("qgemv", qgemv_kernel<QMOE_MXFP4>, grid, kBlock, lds, s, P);
-    case QMOE_Q4_K: return QMOE_LAUNCH("qgemv", qgemv_kernel<QMOE_Q4_K>, grid, kBlock, lds, s, P);
-    default: return QMOE_LAUNCH("qgemv", qgemv_kernel<QMOE_Q6_K>, grid, kBlock, lds, s, P);
+    case QMOE_Q8_0: return qgemv_dispatch<QMOE_Q8_0>(P, RC, grid, lds, s);
+    case QMOE_Q4_0: return qgemv_dispatch<QMOE_Q4_0>(P, RC, grid, lds, s);
+    case QMOE_MXFP4: return qgemv_dispatch<QMOE_MXFP4>(P, RC, grid, lds, s);
+    case QMOE_Q4_K: return qgemv_dispatch<QMOE_Q4_K>(P, RC, grid, lds, s);
+    default: return qgemv_dispatch<QMOE_Q6_K>(P, RC, grid, lds, s);
   }
 }
 
+template <int PHASE, bool MFMA>
+static int ffn_dispatch2(const FfnParams& P, int RC, dim3 grid, size_t lds, hipStream_t s) {
+  const char* name = PHASE == 0 ? "ffn_gate_up" : "ffn_down";
+  if (RC == 1) return QMOE_LAUNCH(name, (ffn_decode_kernel<PHASE, 1, MFMA>), grid, kBlock, lds, s, P);
+  if (RC == 2) return QMOE_LAUNCH(name, (ffn_decode_kernel<PHASE, 2, MFMA>), grid, kBlock, lds, s, P);
+  return QMOE_LAUNCH(name, (ffn_decode_kernel<PHASE, 4, MFMA>), grid, kBlock, lds, s, P);
+}
+
+template <int PHASE>
+static int ffn_dispatch(const FfnParams& P, int RC, dim3 grid, size_t lds, hipStream_t s) {
+  return P.m_max < 0x7FFFFFFF ? ffn_dispatch2<PHASE, true>(P, RC, grid, lds, s)
+                              : ffn_dispatch2<PHASE, false>(P, RC, grid, lds, s);
+}
+
 int validate_tiers(const qmoe_tier* tiers, int n_tiers, int E, int H, int F, bool prefill);
+
+// LDS budget for staged activation rows in the routed FFN (keeps >= 4 blocks
+// resident per CU).
+constexpr size_t kFfnStageBudget = 32768;
 
 }  // namespace qmoe
 
@@ -462,6 +876,7 @@ int moe_ffn_tiered(const qmoe_tier* tiers, int n_tiers, int E, int H, int F, con
   if (T == 0 || k == 0) return QMOE_OK;
   int st = validate_tiers(tiers, n_tiers, E, H, F, false);
   if (st) return st;
+  if (E > 8192) return fail(QMOE_ERR_UNSUPPORTED, "moe_ffn_tiered: E=%d > 8192", E);
   if (!x || !offsets || !perm || !o)
     return fail(QMOE_ERR_INVALID_ARG, "moe_ffn_tiered: null pointer");
   if (x_dtype != QMOE_F32 && x_dtype != QMOE_BF16)
@@ -474,29 +889,42 @@ int moe_ffn_tiered(const qmoe_tier* tiers, int n_tiers, int E, int H, int F, con
                 ws_bytes, need);
   const long long A = (long long)T * k;
   if (A > (1 << 24)) return fail(QMOE_ERR_UNSUPPORTED, "moe_ffn_tiered: T*k too large");
+  const int rc1 = pick_rc(T, H, kFfnStageBudget), rc2 = pick_rc(T, F, kFfnStageBudget);
+  if (!rc1 || !rc2) return fail(QMOE_ERR_UNSUPPORTED, "moe_ffn_tiered: H or F too large");
   hipStream_t s = (hipStream_t)stream;
   FfnParams P{};
   for (int i = 0; i < n_tiers; ++i) P.tiers[i] = tiers[i];
   P.n_tiers = n_tiers; P.E = E; P.H = H; P.F = F; P.T = T; P.k = k;
   P.x = x; P.x_dtype = x_dtype; P.offsets = offsets; P.perm = perm;
   P.h = (float*)ws; P.o = o;
-  // phase 0: gate/up over K = H, rows = F
-  P.G = lanes_per_row(H);
-  chunking(T, H, P.G, P.rcl, P.kc);
-  int rpb = kWaves * (64 / P.G);
-  P.ntiles = (F + rpb - 1) / rpb;
-  if (A * (long long)((H + 3) / 4) >= (1LL << 31) || A * (long long)P.ntiles >= (1LL << 31))
-    return fail(QMOE_ERR_UNSUPPORTED, "moe_ffn_tiered: grid too large");
-  st = QMOE_LAUNCH("ffn_gate_up", ffn_decode_kernel<0>, dim3((unsigned)(A * P.ntiles)), kBlock,
-                   smem_bytes(P.rcl, P.kc), s, P);
-  if (st) return st;
-  // phase 1: down over K = F, rows = H
-  P.G = lanes_per_row(F);
-  chunking(T, F, P.G, P.rcl, P.kc);
-  rpb = kWaves * (64 / P.G);
-  P.ntiles = (H + rpb - 1) / rpb;
-  return QMOE_LAUNCH("ffn_down", ffn_decode_kernel<1>, dim3((unsigned)(A * P.ntiles)), kBlock,
-                     smem_bytes(P.rcl, P.kc), s, P);
+  const int ranks = (int)(A < E ? A : E);  // experts that can receive rows
+  const size_t sched_bytes = (size_t)(E + 1 + 2 * kWaves + 2) * 4;
+  // Experts with more rows than the dot-product path blocks in registers
+  // use the matrix cores, when the row count allows that to happen (with
+  // duplicate ids the dot-product path loops over row chunks instead).
+  for (int phase = 0; phase < 2; ++phase) {
+    const int N = phase == 0 ? F : H, K = phase == 0 ? H : F, rc = phase == 0 ? rc1 : rc2;
+    P.G = lanes_per_row(K);
+    P.tile_rows = pick_tile_rows(N, P.G, ranks);
+    P.ntiles = (N + P.tile_rows - 1) / P.tile_rows;
+    P.m_max = T > rc ? rc : 0x7FFFFFFF;
+    // A many-row expert gets up to (m_max + 1) * ntiles blocks and holds at
+    // least m_max + 1 of the A row assignments, so no routing needs more
+    // than min(A * ntiles, E * max(ntiles, ntiles_big)) blocks.
+    const long long big_cap = (long long)(rc + 1) * P.ntiles, cols16 = (N + 15) / 16;
+    P.ntiles_big = (int)(big_cap < cols16 ? big_cap : cols16);
+    const long long need_a = A * P.ntiles;
+    const long long need_e = (long long)E * (P.ntiles > P.ntiles_big ? P.ntiles : P.ntiles_big);
+    const long long nblocks = need_a < need_e ? need_a : need_e;
+    if (nblocks >= (1LL << 31)) return fail(QMOE_ERR_UNSUPPORTED, "moe_ffn_tiered: grid too large");
+    size_t lds = stage_bytes(rc, K);
+    if (lds < sched_bytes) lds = sched_bytes;
+    if (lds < mfma_red_bytes(2 - phase)) lds = mfma_red_bytes(2 - phase);
+    const dim3 grid((unsigned)nblocks);
+    st = phase == 0 ? ffn_dispatch<0>(P, rc, grid, lds, s) : ffn_dispatch<1>(P, rc, grid, lds, s);
+    if (st) return st;
+  }
+  return QMOE_OK;
 }
 
 }  // extern "C"

@@ -20,12 +20,9 @@
 //  Pass 1 (NMAT = 2): gate and up tiles, SiLU(g) * u -> h (bf16, workspace).
 //  Pass 2 (NMAT = 1): down tiles over K = F -> o (fp32, permuted rows).
 #include "common.hpp"
+#include "dequant.hpp"
 
 namespace qmoe {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kPW = 4;              // waves per block
 constexpr int kPB = 64 * kPW;       // threads per block
@@ -41,124 +38,12 @@ struct PrefillParams {
   const int32_t* offsets;
   const int32_t* perm;
   const int32_t* tile_off;  // [E+1] prefix sum of 64-row tiles per expert
-  uint16_t* h;              // [T*k, F] bf16
+  uint16_t* h;              // [T*k, F] bf16 (prefill)
+  float* h32;               // [T*k, F] fp32 (decode)
   float* o;                 // [T*k, H]
   int ntiles;               // column tiles of this pass
+  int m_min;                // decode: only experts with more rows than this
 };
-
-// byte I of x as a float (selected into v_cvt_f32_ubyteI)
-template <int I>
-QMOE_D float ubyte(uint32_t x) { return (float)((x >> (8 * I)) & 0xFFu); }
-
-QMOE_D uint32_t pack_bf16(float lo, float hi) {
-  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
-  return __builtin_bit_cast(uint32_t, v);
-}
-
-// Dequantize unit u (32 values) of weight row `row` of a [N, K] tensor into
-// 16 words of bf16 pairs in natural element order (word w = elements 2w,
-// 2w+1).  Units at or beyond K give zeros.
-template <int FMT>
-QMOE_D void dequant_unit_bf16(const uint8_t* base, int N, int K, int row, int u, uint32_t out[16]) {
-  if (row >= N || 32 * u >= K) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) out[i] = 0u;
-    return;
-  }
-  const Layout L = layout_of(FMT, N, K);
-  const uint8_t* p0 = base + L.off[0];
-  const uint8_t* p1 = base + L.off[1];
-  const size_t nb32 = (size_t)(K >> 5);
-  if constexpr (FMT == QMOE_Q8_0) {
-    const uint4* q = (const uint4*)(p0 + (size_t)row * K + 32 * (size_t)u);
-    const uint4 a = q[0], b = q[1];
-    const float d = f16_bits_to_f32(((const uint16_t*)p1)[row * nb32 + u]);
-    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const uint32_t ww = w[c] ^ 0x80808080u;  // q + 128
-      const float bias = -128.f * d;
-      out[2 * c] = pack_bf16(fmaf(ubyte<0>(ww), d, bias),
-                             fmaf(ubyte<1>(ww), d, bias));
-      out[2 * c + 1] = pack_bf16(fmaf(ubyte<2>(ww), d, bias),
-                                 fmaf(ubyte<3>(ww), d, bias));
-    }
-  } else if constexpr (FMT == QMOE_MXFP4) {
-    const uint4 q = *(const uint4*)(p0 + (size_t)row * (K >> 1) + 16 * (size_t)u);
-    const float scale = e8m0_to_f32(p1[row * nb32 + u]);
-    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      out[4 * c + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[c], scale, 0));
-      out[4 * c + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[c], scale, 1));
-      out[4 * c + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[c], scale, 2));
-      out[4 * c + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[c], scale, 3));
-    }
-  } else if constexpr (FMT == QMOE_Q4_0 || FMT == QMOE_Q4_K) {
-    const uint4 q = *(const uint4*)(p0 + (size_t)row * (K >> 1) + 16 * (size_t)u);
-    float a, b;  // value = a * q + b
-    if constexpr (FMT == QMOE_Q4_0) {
-      a = f16_bits_to_f32(((const uint16_t*)p1)[row * nb32 + u]);
-      b = -8.f * a;
-    } else {
-      const uint4 meta = ((const uint4*)p1)[(size_t)row * (K >> 8) + (u >> 3)];
-      const int j = u & 7;
-      const uint64_t lo = (uint64_t)meta.y | ((uint64_t)meta.z << 32);
-      const uint64_t hi = (uint64_t)meta.z | ((uint64_t)meta.w << 32);
-      a = f16_bits_to_f32(meta.x & 0xFFFFu) * (float)((lo >> (6 * j)) & 63u);
-      b = -f16_bits_to_f32(meta.x >> 16) * (float)((hi >> (16 + 6 * j)) & 63u);
-    }
-    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint32_t lo4 = w[c] & 0x0F0F0F0Fu;         // elements 8c, 8c+2, 8c+4, 8c+6
-      const uint32_t hi4 = (w[c] >> 4) & 0x0F0F0F0Fu;  // elements 8c+1, 8c+3, ...
-      out[4 * c + 0] = pack_bf16(fmaf(ubyte<0>(lo4), a, b),
-                                 fmaf(ubyte<0>(hi4), a, b));
-      out[4 * c + 1] = pack_bf16(fmaf(ubyte<1>(lo4), a, b),
-                                 fmaf(ubyte<1>(hi4), a, b));
-      out[4 * c + 2] = pack_bf16(fmaf(ubyte<2>(lo4), a, b),
-                                 fmaf(ubyte<2>(hi4), a, b));
-      out[4 * c + 3] = pack_bf16(fmaf(ubyte<3>(lo4), a, b),
-                                 fmaf(ubyte<3>(hi4), a, b));
-    }
-  } else {  // Q6_K
-    const uint4 ql = *(const uint4*)(p0 + (size_t)row * (K >> 1) + 16 * (size_t)u);
-    const uint2 qh = *(const uint2*)(p1 + (size_t)row * (K >> 2) + 8 * (size_t)u);
-    const size_t sb = (size_t)row * (K >> 8) + (u >> 3);
-    const uint32_t sc2 = ((const uint16_t*)(base + L.off[2] + 16 * sb))[u & 7];
-    const float d = f16_bits_to_f32(((const uint16_t*)(base + L.off[3]))[sb]);
-    const float a0 = d * (float)(int8_t)(sc2 & 0xFFu), a1 = d * (float)(int8_t)(sc2 >> 8);
-    const uint32_t w[4] = {ql.x, ql.y, ql.z, ql.w};
-    const uint32_t hw[2] = {qh.x, qh.y};
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      // 8 elements 8c..8c+7: low nibbles in w[c], high bit pairs in 16 bits of qh
-      const uint32_t h16 = (hw[c >> 1] >> (16 * (c & 1))) & 0xFFFFu;
-      const float a = c < 2 ? a0 : a1;
-      const float b = -32.f * a;
-      // byte i of q6 holds element 8c+2i (even) / 8c+2i+1 (odd) codes
-      const uint32_t lo_e = (w[c] & 0x0F0F0F0Fu);
-      const uint32_t lo_o = (w[c] >> 4) & 0x0F0F0F0Fu;
-      // high bits: element 8c+m at bits 2m of h16
-      uint32_t he = 0, ho = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        he |= ((h16 >> (4 * i)) & 3u) << (8 * i + 4);
-        ho |= ((h16 >> (4 * i + 2)) & 3u) << (8 * i + 4);
-      }
-      const uint32_t ce = lo_e | he, co = lo_o | ho;
-      out[4 * c + 0] = pack_bf16(fmaf(ubyte<0>(ce), a, b),
-                                 fmaf(ubyte<0>(co), a, b));
-      out[4 * c + 1] = pack_bf16(fmaf(ubyte<1>(ce), a, b),
-                                 fmaf(ubyte<1>(co), a, b));
-      out[4 * c + 2] = pack_bf16(fmaf(ubyte<2>(ce), a, b),
-                                 fmaf(ubyte<2>(co), a, b));
-      out[4 * c + 3] = pack_bf16(fmaf(ubyte<3>(ce), a, b),
-                                 fmaf(ubyte<3>(co), a, b));
-    }
-  }
-}
 
 // The (expert, tile) of schedule slot i, or e = -1.
 QMOE_D int tile_expert(const int32_t* tile_off, int E, int i, int& mt) {
@@ -172,66 +57,80 @@ QMOE_D int tile_expert(const int32_t* tile_off, int E, int i, int& mt) {
   return lo;
 }
 
-QMOE_D const qmoe_tier* prefill_tier(const PrefillParams& P, int e) {
-  for (int i = 0; i < P.n_tiers; ++i)
-    if (e >= P.tiers[i].e_begin && e < P.tiers[i].e_end) return &P.tiers[i];
-  return nullptr;
+// The tier holding expert e, assembled field by field with constant indices
+// only (a runtime index or struct copy out of the by-value kernel argument
+// would spill the whole argument block to scratch).
+QMOE_D bool prefill_tier(const PrefillParams& P, int e, qmoe_tier& out) {
+  bool found = false;
+  int32_t eb = 0, ee = 0, fgu = 0, fd = 0;
+  const void *g = nullptr, *u = nullptr, *d = nullptr;
+#pragma unroll
+  for (int i = 0; i < QMOE_MAX_TIERS; ++i) {
+    const bool hit = !found && i < P.n_tiers && e >= P.tiers[i].e_begin && e < P.tiers[i].e_end;
+    if (hit) {
+      eb = P.tiers[i].e_begin; ee = P.tiers[i].e_end;
+      fgu = P.tiers[i].fmt_gate_up; fd = P.tiers[i].fmt_down;
+      g = P.tiers[i].gate; u = P.tiers[i].up; d = P.tiers[i].down;
+      found = true;
+    }
+  }
+  out.e_begin = eb; out.e_end = ee; out.fmt_gate_up = fgu; out.fmt_down = fd;
+  out.gate = g; out.up = u; out.down = d;
+  return found;
 }
 
-// Stage rows 0..63 of the tile, values k0 .. k0+255, as bf16 into As.
-// PASS 1: x rows gathered by token; PASS 2: h rows (bf16) by position.
-template <int PASS>
+// Stage rows 0 .. 16*MI-1 of a tile, values k0 .. k0+255, into As as bf16
+// (prefill) or fp16 (DEC, decode rows); rows >= cnt and values >= K are zero.
+// PASS 1: x rows gathered by token; PASS 2: h rows by position (bf16 for
+// prefill, fp32 in the decode workspace).
+template <int PASS, int MI, bool DEC>
 QMOE_D void stage_tile(const PrefillParams& P, uint16_t* As, int pos0, int cnt, int K, int k0) {
-  const int r = threadIdx.x >> 2, part = threadIdx.x & 3;  // 64 values per thread
-  uint32_t w[32];
-  const int kk = k0 + 64 * part;
-  if (r < cnt && kk < K) {
-    const int pos = pos0 + r;
-    if (PASS == 1) {
-      const int tok = P.perm[pos] / P.k;
-      if (P.x_dtype == QMOE_F32) {
-        const float4* src = (const float4*)((const float*)P.x + (size_t)tok * K + kk);
+  constexpr int ROWS = 16 * MI, CH = kBK / 8;  // 8-value chunks per row
+  for (int idx = threadIdx.x; idx < ROWS * CH; idx += kPB) {
+    const int r = idx / CH, c = idx - r * CH;
+    const int kk = k0 + 8 * c;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (r < cnt && kk < K) {
+      const int pos = pos0 + r;
+      if (PASS == 1) {
+        const int tok = P.perm[pos] / P.k;
+        if (P.x_dtype == QMOE_F32) {
+          const float4* src = (const float4*)((const float*)P.x + (size_t)tok * K + kk);
+          const float4 a = src[0], b = src[1];
+          v = make_uint4(pack2<DEC>(a.x, a.y), pack2<DEC>(a.z, a.w), pack2<DEC>(b.x, b.y),
+                         pack2<DEC>(b.z, b.w));
+        } else {
+          v = *(const uint4*)((const uint16_t*)P.x + (size_t)tok * K + kk);
+          if (DEC) {  // bf16 -> fp16
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+            uint32_t o[4];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float4 f = src[i];
-          w[2 * i] = pack_bf16(f.x, f.y);
-          w[2 * i + 1] = pack_bf16(f.z, f.w);
+            for (int j = 0; j < 4; ++j)
+              o[j] = pack_f16(bf16_bits_to_f32(w[j] & 0xFFFFu), bf16_bits_to_f32(w[j] >> 16));
+            v = make_uint4(o[0], o[1], o[2], o[3]);
+          }
         }
+      } else if (DEC) {
+        const float4* src = (const float4*)(P.h32 + (size_t)pos * K + kk);
+        const float4 a = src[0], b = src[1];
+        v = make_uint4(pack_f16(a.x, a.y), pack_f16(a.z, a.w), pack_f16(b.x, b.y),
+                       pack_f16(b.z, b.w));
       } else {
-        const uint4* src = (const uint4*)((const uint16_t*)P.x + (size_t)tok * K + kk);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint4 b = src[i];
-          w[4 * i] = b.x; w[4 * i + 1] = b.y; w[4 * i + 2] = b.z; w[4 * i + 3] = b.w;
-        }
-      }
-    } else {
-      const uint4* src = (const uint4*)(P.h + (size_t)pos * K + kk);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint4 b = src[i];
-        w[4 * i] = b.x; w[4 * i + 1] = b.y; w[4 * i + 2] = b.z; w[4 * i + 3] = b.w;
+        v = *(const uint4*)(P.h + (size_t)pos * K + kk);
       }
     }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 32; ++i) w[i] = 0u;
+    *(uint4*)(As + r * kAStride + 8 * c) = v;
   }
-  uint4* dst = (uint4*)(As + r * kAStride + 64 * part);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) dst[i] = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
 }
 
-// One block: rows of tile mt of expert e x columns [n0, n0 + 4*NB*16).
-template <int FMT, int PASS, int NB>
-QMOE_D void prefill_tile(const PrefillParams& P, const qmoe_tier* t, int e, int mt, int nt,
-                         uint16_t* As) {
+// One block: rows pos0 .. pos0+cnt-1 (cnt <= 16*MI) of expert e's permuted
+// positions x columns [n0, n0 + 4*NB*16) of column tile nt.
+template <int FMT, int PASS, int NB, int MI, bool DEC>
+QMOE_D void mfma_tile(const PrefillParams& P, const qmoe_tier* t, int e, int pos0, int cnt,
+                      int nt, uint16_t* As) {
   constexpr int NMAT = PASS == 1 ? 2 : 1;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, li = lane & 15;
-  const int m_e = P.offsets[e + 1] - P.offsets[e];
-  const int pos0 = P.offsets[e] + mt * kBM;
-  const int cnt = min(kBM, m_e - mt * kBM);
   const int nmi = (cnt + 15) >> 4;
   const int N = PASS == 1 ? P.F : P.H;
   const int K = PASS == 1 ? P.H : P.F;
@@ -241,17 +140,17 @@ QMOE_D void prefill_tile(const PrefillParams& P, const qmoe_tier* t, int e, int 
   const uint8_t* W1 = (const uint8_t*)t->up + eo;
   const int n0 = nt * (kPW * NB * 16) + wave * (NB * 16);
 
-  f32x4_t acc[NB][NMAT][4];
+  f32x4_t acc[NB][NMAT][MI];
 #pragma unroll
   for (int b = 0; b < NB; ++b)
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[b][m][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < MI; ++i) acc[b][m][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   for (int k0 = 0; k0 < K; k0 += kBK) {
     __syncthreads();
-    stage_tile<PASS>(P, As, pos0, cnt, K, k0);
+    stage_tile<PASS, MI, DEC>(P, As, pos0, cnt, K, k0);
     __syncthreads();
     const int u0 = (k0 >> 5) + g;
 #pragma unroll
@@ -260,28 +159,33 @@ QMOE_D void prefill_tile(const PrefillParams& P, const qmoe_tier* t, int e, int 
       uint32_t wb[NMAT][2][16];
 #pragma unroll
       for (int m = 0; m < NMAT; ++m) {
-        dequant_unit_bf16<FMT>(m == 0 ? W0 : W1, N, K, row, u0, wb[m][0]);
-        dequant_unit_bf16<FMT>(m == 0 ? W0 : W1, N, K, row, u0 + 4, wb[m][1]);
+        dequant_unit<FMT, DEC>(m == 0 ? W0 : W1, N, K, row, u0, wb[m][0]);
+        dequant_unit<FMT, DEC>(m == 0 ? W0 : W1, N, K, row, u0 + 4, wb[m][1]);
       }
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         const int half = s >> 2, q = s & 3;  // unit g (+4 for half 1), values 8q..8q+7
         const int acol = 128 * half + 32 * g + 8 * q;
-        bf16x8_t bop[NMAT];
+        uint4 bop[NMAT];
 #pragma unroll
-        for (int m = 0; m < NMAT; ++m) {
-          const uint4 v = make_uint4(wb[m][half][4 * q], wb[m][half][4 * q + 1],
-                                     wb[m][half][4 * q + 2], wb[m][half][4 * q + 3]);
-          bop[m] = __builtin_bit_cast(bf16x8_t, v);
-        }
+        for (int m = 0; m < NMAT; ++m)
+          bop[m] = make_uint4(wb[m][half][4 * q], wb[m][half][4 * q + 1],
+                              wb[m][half][4 * q + 2], wb[m][half][4 * q + 3]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < MI; ++i) {
           if (i < nmi) {
             const uint4 av = *(const uint4*)(As + (16 * i + li) * kAStride + acol);
-            const bf16x8_t aop = __builtin_bit_cast(bf16x8_t, av);
 #pragma unroll
-            for (int m = 0; m < NMAT; ++m)
-              acc[b][m][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bop[m], acc[b][m][i], 0, 0, 0);
+            for (int m = 0; m < NMAT; ++m) {
+              if constexpr (DEC)
+                acc[b][m][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                    __builtin_bit_cast(f16x8_t, av), __builtin_bit_cast(f16x8_t, bop[m]),
+                    acc[b][m][i], 0, 0, 0);
+              else
+                acc[b][m][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, bop[m]),
+                    acc[b][m][i], 0, 0, 0);
+            }
           }
         }
       }
@@ -293,7 +197,7 @@ QMOE_D void prefill_tile(const PrefillParams& P, const qmoe_tier* t, int e, int 
     const int col = n0 + b * 16 + li;
     if (col >= N) continue;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < MI; ++i) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = 16 * i + 4 * g + j;
@@ -302,12 +206,27 @@ QMOE_D void prefill_tile(const PrefillParams& P, const qmoe_tier* t, int e, int 
         if constexpr (PASS == 1) {
           const float gv = acc[b][0][i][j], uv = acc[b][1][i][j];
           const float hv = gv / (1.f + expf(-gv)) * uv;
-          P.h[pos * P.F + col] = (uint16_t)(pack_bf16(hv, 0.f) & 0xFFFFu);
+          if (DEC) P.h32[pos * P.F + col] = hv;
+          else P.h[pos * P.F + col] = (uint16_t)(pack_bf16(hv, 0.f) & 0xFFFFu);
         } else {
           P.o[pos * P.H + col] = acc[b][0][i][j];
         }
       }
     }
+  }
+}
+
+template <int PASS, int MI, bool DEC, int NB>
+QMOE_D void mfma_dispatch(const PrefillParams& P, const qmoe_tier* t, int e, int pos0, int cnt,
+                          int nt, uint16_t* As) {
+  const int fmt = PASS == 1 ? t->fmt_gate_up : t->fmt_down;
+  switch (fmt) {
+    case QMOE_Q8_0: mfma_tile<QMOE_Q8_0, PASS, NB, MI, DEC>(P, t, e, pos0, cnt, nt, As); break;
+    case QMOE_Q4_0: mfma_tile<QMOE_Q4_0, PASS, NB, MI, DEC>(P, t, e, pos0, cnt, nt, As); break;
+    case QMOE_MXFP4: mfma_tile<QMOE_MXFP4, PASS, NB, MI, DEC>(P, t, e, pos0, cnt, nt, As); break;
+    case QMOE_Q4_K: mfma_tile<QMOE_Q4_K, PASS, NB, MI, DEC>(P, t, e, pos0, cnt, nt, As); break;
+    case QMOE_Q6_K: mfma_tile<QMOE_Q6_K, PASS, NB, MI, DEC>(P, t, e, pos0, cnt, nt, As); break;
+    default: break;
   }
 }
 
@@ -318,17 +237,13 @@ __global__ __launch_bounds__(kPB) void prefill_kernel(PrefillParams P) {
   int mt = 0;
   const int e = tile_expert(P.tile_off, P.E, i, mt);
   if (e < 0) return;
-  const qmoe_tier* t = prefill_tier(P, e);
-  if (!t) return;
-  const int fmt = PASS == 1 ? t->fmt_gate_up : t->fmt_down;
-  switch (fmt) {
-    case QMOE_Q8_0: prefill_tile<QMOE_Q8_0, PASS, NB>(P, t, e, mt, nt, As); break;
-    case QMOE_Q4_0: prefill_tile<QMOE_Q4_0, PASS, NB>(P, t, e, mt, nt, As); break;
-    case QMOE_MXFP4: prefill_tile<QMOE_MXFP4, PASS, NB>(P, t, e, mt, nt, As); break;
-    case QMOE_Q4_K: prefill_tile<QMOE_Q4_K, PASS, NB>(P, t, e, mt, nt, As); break;
-    case QMOE_Q6_K: prefill_tile<QMOE_Q6_K, PASS, NB>(P, t, e, mt, nt, As); break;
-    default: break;
-  }
+  qmoe_tier tier;
+  if (!prefill_tier(P, e, tier)) return;
+  const qmoe_tier* t = &tier;
+  const int m_e = P.offsets[e + 1] - P.offsets[e];
+  const int pos0 = P.offsets[e] + mt * kBM;
+  const int cnt = min(kBM, m_e - mt * kBM);
+  mfma_dispatch<PASS, kBM / 16, false, NB>(P, t, e, pos0, cnt, nt, As);
 }
 
 // tile_off[e] = sum over e' < e of ceil(m_e' / 64), one block.

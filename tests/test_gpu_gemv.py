@@ -11,7 +11,12 @@ from decode_moe_mul_amd import configs, layers, qmoe, synth
 pytestmark = [pytest.mark.gpu, requires_gpu]
 
 
-def _grid_fields(fmt, N, K, rng):
+def _grid_fields(fmt, N, K, rng, fp16_exact=False):
+    """Quantized fields whose dequantized values are exact in fp32.  With
+    fp16_exact (many activation rows run on the fp16 matrix cores) every
+    weight value is also exact in fp16: the Q4_K min scale equals the block
+    scale, so d*sc*q - dmin*m is an integer multiple of d below 2^11, and the
+    Q6_K sub-block scales stay within +-63 so |sc*(q-32)| <= 2016."""
     nb = K // fm.BLOCK[fmt]
     p2 = lambda: np.float16(2.0 ** -int(rng.integers(3, 8)))
     if fmt == "q8_0":
@@ -24,13 +29,15 @@ def _grid_fields(fmt, N, K, rng):
         return {"q": rng.integers(0, 16, (N, K)).astype(np.uint8),
                 "e": rng.integers(120, 128, (N, nb)).astype(np.uint8)}
     if fmt == "q4_k":
-        return {"q": rng.integers(0, 16, (N, K)).astype(np.uint8),
-                "d": np.array([[p2() for _ in range(nb)] for _ in range(N)], np.float16),
-                "dmin": np.array([[p2() for _ in range(nb)] for _ in range(N)], np.float16),
+        d = np.array([[p2() for _ in range(nb)] for _ in range(N)], np.float16)
+        dmin = d.copy() if fp16_exact else \
+            np.array([[p2() for _ in range(nb)] for _ in range(N)], np.float16)
+        return {"q": rng.integers(0, 16, (N, K)).astype(np.uint8), "d": d, "dmin": dmin,
                 "sc": rng.integers(0, 64, (N, nb, 8)).astype(np.uint8),
                 "m": rng.integers(0, 64, (N, nb, 8)).astype(np.uint8)}
+    lim = 64 if fp16_exact else 128
     return {"q": rng.integers(0, 64, (N, K)).astype(np.uint8),
-            "sc": rng.integers(-128, 128, (N, nb, 16)).astype(np.int8),
+            "sc": rng.integers(-lim + 1, lim, (N, nb, 16)).astype(np.int8),
             "d": np.array([[p2() for _ in range(nb)] for _ in range(N)], np.float16)}
 
 
@@ -42,7 +49,7 @@ def test_gemv_grid_exact_is_bitexact(fmt, R):
     result, which the oracle computes in float64."""
     N, K = 77, 1024
     rng = np.random.default_rng(R)
-    buf = fm.pack(fmt, _grid_fields(fmt, N, K, rng), N, K)
+    buf = fm.pack(fmt, _grid_fields(fmt, N, K, rng, fp16_exact=R > 4), N, K)
     x = rng.integers(-4, 5, (R, K)).astype(np.float32)
     y_ref, _ = moe.gemv(fmt, buf, N, K, x)
     y = to_np(qmoe.gemv(fmt, to_gpu(buf), N, K, to_gpu(x)))
