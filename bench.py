@@ -116,13 +116,93 @@ def cpu_baseline(budget_s=20.0):
                       f"dequantize-then-dot ({elapsed:.1f}s; {done / elapsed:.2f} tokens/s)"}
 
 
+# ------------------------------------------------------------------ traffic --
+# HBM traffic of the dominant kernel comes from two rocprofv3 counter runs of
+# this script (FETCH_SIZE, then WRITE_SIZE).  Every run copies CAL_BYTES once
+# with a plain device copy before the timed region; the counters that copy
+# reports calibrate the KiB units.  The summary is stored with a hash of the
+# kernel sources and ignored once they change.
+CAL_BYTES = 256 << 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ffn_gate_up_traffic.json")
+KERNEL_SOURCES = ("decode_moe_mul_amd/csrc/gemv.hip", "decode_moe_mul_amd/csrc/common.hpp")
+
+
+def kernel_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic():
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_hash") != kernel_hash():
+        return None
+    return t
+
+
+def _pmc_rows(d):
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    if not rows:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    return rows
+
+
+def _per_dispatch(rows, counter, pick):
+    vals = {}
+    for r in rows:
+        if r.get("Counter_Name") != counter or not pick(r):
+            continue
+        key = r.get("Dispatch_Id") or r.get("Correlation_Id")
+        vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+    return vals
+
+
+def summarize_pmc(fetch_dir, write_dir):
+    """Write TRAFFIC_FILE from the two counter runs."""
+    is_gu = lambda r: "ffn_decode_kernel<0" in r["Kernel_Name"]
+    # the calibration copy: the last large runtime copy of the program (the
+    # later ones are small reads of routing results)
+    is_copy = lambda r: "copyBuffer" in r["Kernel_Name"] and int(r["Grid_Size"]) >= 65536
+    out = {"kernel_hash": kernel_hash(), "cal_bytes": CAL_BYTES}
+    for name, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
+        rows = _pmc_rows(d)
+        gu = _per_dispatch(rows, counter, is_gu)
+        cp = _per_dispatch(rows, counter, is_copy)
+        cal = cp[max(cp, key=int)]  # KiB the counter reports for CAL_BYTES
+        out[f"{name}_cal_kib"] = cal
+        out[f"{name}_kib_per_launch"] = sum(gu.values()) / len(gu)
+        out[f"{name}_bytes_per_launch"] = sum(gu.values()) / len(gu) * CAL_BYTES / cal
+        out[f"{name}_launches"] = len(gu)
+    out["traffic_bytes_per_launch"] = out["fetch_bytes_per_launch"] + out["write_bytes_per_launch"]
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the traffic summary from two rocprofv3 --pmc runs and exit")
     a = ap.parse_args()
+    if a.summarize_pmc:
+        summarize_pmc(*a.summarize_pmc)
+        return
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; the decode path has "
                                    "no multi-GPU mode (run with --gpus 1)"}))
@@ -149,6 +229,13 @@ def main():
                                                 layer.cfg.F, layer.cfg.H) for e in flat)
         per_step_bytes.append(b_step)
         gate_up_bytes.append(g_step)
+
+    # calibration copy for the traffic counters (outside the timed region)
+    cal_src = torch.empty(CAL_BYTES // 4, dtype=torch.float32, device="cuda")
+    cal_dst = torch.empty_like(cal_src)
+    cal_dst.copy_(cal_src)
+    torch.cuda.synchronize()
+    del cal_src, cal_dst
 
     for s in range(a.warmup):
         for layer, x, copy, rows in step_calls(tiered, grouped, xt, xg, s):
@@ -180,6 +267,8 @@ def main():
     kernel_ms = {k: qmoe.profile_read(k) for k in
                  ("router_gemv", "topk", "permute", "ffn_gate_up", "ffn_down", "combine")}
 
+    t = stored_traffic()
+    traffic = None if t is None else int(t["traffic_bytes_per_launch"])
     total_bytes = float(np.sum(per_step_bytes))
     gbs = total_bytes / (total_ms * 1e-3) / 1e9
     gu_gbs = float(np.sum(gate_up_bytes)) / (gu_ms * 1e-3) / 1e9
@@ -210,7 +299,7 @@ def main():
         "kernel_ms_per_step": {k: round(v[1] / a.steps, 5) for k, v in kernel_ms.items()},
         "roofline": {"bound": "hbm", "kernel": "ffn_gate_up",
                      "achieved": round(gu_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "launches": n_gu,
                      "avg_launch_us": round(gu_ms * 1e3 / max(n_gu, 1), 3),
                      "algorithmic_bytes_per_launch": int(np.sum(gate_up_bytes) / max(n_gu, 1))},

@@ -177,15 +177,24 @@ QMOE_D void bytes_to_h2(const uint4 a, const uint4 b, uint32_t out[16]) {
 
 // Q4_0 / Q4_K nibbles: pair 4c+j = (1024 + e, 1024 + e') for even j and
 // (1024 + 16e, 1024 + 16e') for odd j, e = element 8c+j, e' = element 8c+j+4.
+// (x & mask) | bits in one instruction.  The compiler splits this pattern
+// into an and plus an or when the operands are constants, so the operation
+// is written out; mask comes in a scalar register, bits in a vector one.
+QMOE_D uint32_t and_or(uint32_t x, uint32_t mask, uint32_t bits) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(mask), "v"(bits));
+  return r;
+}
+
 QMOE_D void nibbles_biased(const uint4 q, uint32_t out[16]) {
   const uint32_t w[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const uint32_t t = w[c] >> 8;
-    out[4 * c + 0] = (w[c] & 0x000F000Fu) | H2_MAGIC;
-    out[4 * c + 1] = (w[c] & 0x00F000F0u) | H2_MAGIC;
-    out[4 * c + 2] = (t & 0x000F000Fu) | H2_MAGIC;
-    out[4 * c + 3] = (t & 0x00F000F0u) | H2_MAGIC;
+    out[4 * c + 0] = and_or(w[c], 0x000F000Fu, H2_MAGIC);
+    out[4 * c + 1] = and_or(w[c], 0x00F000F0u, H2_MAGIC);
+    out[4 * c + 2] = and_or(t, 0x000F000Fu, H2_MAGIC);
+    out[4 * c + 3] = and_or(t, 0x00F000F0u, H2_MAGIC);
   }
 }
 
@@ -199,21 +208,23 @@ QMOE_D void q6_biased(const uint4 ql, const uint2 qh, uint32_t out[16]) {
     // high bits of elements 8c+j and 8c+j+4 at bits 2j and 16+2j
     const uint32_t hh = (hw[c] & 0xFFu) | ((hw[c] & 0xFF00u) << 8);
     const uint32_t t = w[c] >> 8;
-    out[4 * c + 0] = (w[c] & 0x000F000Fu) | ((hh << 4) & 0x00300030u) | H2_MAGIC;
-    out[4 * c + 1] = (w[c] & 0x00F000F0u) | ((hh << 6) & 0x03000300u) | H2_MAGIC;
-    out[4 * c + 2] = (t & 0x000F000Fu) | (hh & 0x00300030u) | H2_MAGIC;
-    out[4 * c + 3] = (t & 0x00F000F0u) | ((hh << 2) & 0x03000300u) | H2_MAGIC;
+    out[4 * c + 0] = and_or(hh << 4, 0x00300030u, and_or(w[c], 0x000F000Fu, H2_MAGIC));
+    out[4 * c + 1] = and_or(hh << 6, 0x03000300u, and_or(w[c], 0x00F000F0u, H2_MAGIC));
+    out[4 * c + 2] = and_or(hh, 0x00300030u, and_or(t, 0x000F000Fu, H2_MAGIC));
+    out[4 * c + 3] = and_or(hh << 2, 0x03000300u, and_or(t, 0x00F000F0u, H2_MAGIC));
   }
 }
 
 // Q8_0 (byte order): 1152 + q for the signed byte q.
 QMOE_D void bytes_biased(const uint4 a, const uint4 b, uint32_t out[16]) {
   const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  // byte permute from {0x64646464 : u}: (byte 0, 0x64, byte 2, 0x64) and
+  // (byte 1, 0x64, byte 3, 0x64), i.e. fp16 1024 + byte in both halves
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
     const uint32_t u = w[c] ^ 0x80808080u;
-    out[2 * c] = (u & 0x00FF00FFu) | H2_MAGIC;
-    out[2 * c + 1] = ((u >> 8) & 0x00FF00FFu) | H2_MAGIC;
+    out[2 * c] = __builtin_amdgcn_perm(0x64646464u, u, 0x04020400u);
+    out[2 * c + 1] = __builtin_amdgcn_perm(0x64646464u, u, 0x04030401u);
   }
 }
 

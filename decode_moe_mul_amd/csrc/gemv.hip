@@ -379,8 +379,22 @@ QMOE_D void valu_rows(const Mat (&mats)[NMAT], int K, int rb, int re, int G, int
     __syncthreads();
     stage_rows<FMT>(xs, sb, rc, U, [&](int r) { return src_of(c0 + r); }, dtype);
     __syncthreads();
-    valu_pass<FMT, NMAT, RC>(mats, K, rb, re, G, rc, xs, sb,
-                             [&](int n, int r, const float* a) { sink_of(n, c0 + r, a); });
+    // the register blocking of the pass follows this chunk's row count, so
+    // an expert with one row does not pay for the dots of RC rows
+    auto sink = [&](int n, int r, const float* a) { sink_of(n, c0 + r, a); };
+    if constexpr (RC >= 4) {
+      if (rc > 2) {
+        valu_pass<FMT, NMAT, 4>(mats, K, rb, re, G, rc, xs, sb, sink);
+        continue;
+      }
+    }
+    if constexpr (RC >= 2) {
+      if (rc == 2) {
+        valu_pass<FMT, NMAT, 2>(mats, K, rb, re, G, rc, xs, sb, sink);
+        continue;
+      }
+    }
+    valu_pass<FMT, NMAT, 1>(mats, K, rb, re, G, rc, xs, sb, sink);
   }
 }
 
@@ -799,15 +813,16 @@ static int qgemv_dispatch(const GemvParams& P, int RC, dim3 grid, size_t lds, hi
 static int qgemv_launch(int FMT, const void* W, int N, int K, const void* x, int x_dtype,
                         int R, float* y, void* stream) {
   if (!W || !x || !y) return fail(QMOE_ERR_INVALID_ARG, "qgemv: null pointer");
-  if (N < 0 || K <= 0 || R < 0 || K % block_of(FMT))
+  if (N < 0 || K <= 0 || R < 0 || K % block_of(FMT) || K > 65536)
     return fail(QMOE_ERR_INVALID_ARG, "qgemv: bad sizes N=%d K=%d R=%d", N, K, R);
   if (x_dtype != QMOE_F32 && x_dtype != QMOE_BF16)
     return fail(QMOE_ERR_UNSUPPORTED, "qgemv: unknown x_dtype %d", x_dtype);
   if (!QMOE_ALIGNED(W, 256) || !QMOE_ALIGNED(x, 16) || !QMOE_ALIGNED(y, 4))
     return fail(QMOE_ERR_INVALID_ARG, "qgemv: misaligned pointer");
-  const int RC = pick_rc(R, K);
-  if (!RC) return fail(QMOE_ERR_UNSUPPORTED, "qgemv: K=%d too large (max 28672)", K);
   if (N == 0 || R == 0) return QMOE_OK;
+  // RC = 0: one staged row does not fit in LDS (K > 27456); such rows (and
+  // more rows than RC) take the matrix-core path, which stages nothing
+  const int RC = pick_rc(R, K);
   GemvParams P{W, N, K, x, x_dtype, R, y, lanes_per_row(K), 0};
   P.tile_rows = pick_tile_rows(N, P.G, 1);
   const dim3 grid((N + P.tile_rows - 1) / P.tile_rows);
@@ -838,9 +853,10 @@ static int ffn_dispatch(const FfnParams& P, int RC, dim3 grid, size_t lds, hipSt
 
 int validate_tiers(const qmoe_tier* tiers, int n_tiers, int E, int H, int F, bool prefill);
 
-// LDS budget for staged activation rows in the routed FFN (keeps >= 4 blocks
-// resident per CU).
-constexpr size_t kFfnStageBudget = 32768;
+// LDS budget for staged activation rows in the routed FFN.  Registers, not
+// LDS, bound the resident blocks of these kernels (2-3 per CU), so a block
+// may take up to the 64 KB a launch can request.
+constexpr size_t kFfnStageBudget = kLdsCap;
 
 }  // namespace qmoe
 
@@ -889,8 +905,9 @@ int moe_ffn_tiered(const qmoe_tier* tiers, int n_tiers, int E, int H, int F, con
                 ws_bytes, need);
   const long long A = (long long)T * k;
   if (A > (1 << 24)) return fail(QMOE_ERR_UNSUPPORTED, "moe_ffn_tiered: T*k too large");
+  // rc = 0: not even one row of that K fits in LDS; then every expert of
+  // that phase takes the matrix-core path (m_max = 0)
   const int rc1 = pick_rc(T, H, kFfnStageBudget), rc2 = pick_rc(T, F, kFfnStageBudget);
-  if (!rc1 || !rc2) return fail(QMOE_ERR_UNSUPPORTED, "moe_ffn_tiered: H or F too large");
   hipStream_t s = (hipStream_t)stream;
   FfnParams P{};
   for (int i = 0; i < n_tiers; ++i) P.tiers[i] = tiers[i];
@@ -907,7 +924,7 @@ int moe_ffn_tiered(const qmoe_tier* tiers, int n_tiers, int E, int H, int F, con
     P.G = lanes_per_row(K);
     P.tile_rows = pick_tile_rows(N, P.G, ranks);
     P.ntiles = (N + P.tile_rows - 1) / P.tile_rows;
-    P.m_max = T > rc ? rc : 0x7FFFFFFF;
+    P.m_max = rc == 0 ? 0 : T > rc ? rc : 0x7FFFFFFF;
     // A many-row expert gets up to (m_max + 1) * ntiles blocks and holds at
     // least m_max + 1 of the A row assignments, so no routing needs more
     // than min(A * ntiles, E * max(ntiles, ntiles_big)) blocks.
@@ -917,11 +934,12 @@ int moe_ffn_tiered(const qmoe_tier* tiers, int n_tiers, int E, int H, int F, con
     const long long need_e = (long long)E * (P.ntiles > P.ntiles_big ? P.ntiles : P.ntiles_big);
     const long long nblocks = need_a < need_e ? need_a : need_e;
     if (nblocks >= (1LL << 31)) return fail(QMOE_ERR_UNSUPPORTED, "moe_ffn_tiered: grid too large");
-    size_t lds = stage_bytes(rc, K);
+    size_t lds = rc ? stage_bytes(rc, K) : 0;
     if (lds < sched_bytes) lds = sched_bytes;
     if (lds < mfma_red_bytes(2 - phase)) lds = mfma_red_bytes(2 - phase);
     const dim3 grid((unsigned)nblocks);
-    st = phase == 0 ? ffn_dispatch<0>(P, rc, grid, lds, s) : ffn_dispatch<1>(P, rc, grid, lds, s);
+    const int rc_t = rc ? rc : 1;  // register blocking of the (unused) dot-product path
+    st = phase == 0 ? ffn_dispatch<0>(P, rc_t, grid, lds, s) : ffn_dispatch<1>(P, rc_t, grid, lds, s);
     if (st) return st;
   }
   return QMOE_OK;

@@ -32,32 +32,76 @@ struct RouteParams {
   int KS, ks_len;
 };
 
+// 4 consecutive activations (fp32 or bf16) starting at element i (i % 4 == 0)
+template <int DT>
+QMOE_D float4 load_act4(const void* x, size_t i) {
+  if constexpr (DT == QMOE_F32) {
+    return *(const float4*)((const float*)x + i);
+  } else {
+    const uint2 b = *(const uint2*)((const uint16_t*)x + i);
+    return make_float4(bf16_bits_to_f32(b.x & 0xFFFFu), bf16_bits_to_f32(b.x >> 16),
+                       bf16_bits_to_f32(b.y & 0xFFFFu), bf16_bits_to_f32(b.y >> 16));
+  }
+}
+
+// x[:, k0:k0+len] -> xsl [T][ks_len], float4 granules, 4 loads in flight
+template <int DT>
+QMOE_D void stage_x_slice(const RouteParams& P, int k0, int len, float* xsl) {
+  const int l4 = len >> 2, n4 = P.T * l4;
+  for (int i0 = threadIdx.x; i0 < n4; i0 += 4 * kRouteBlock) {
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = min(i0 + u * kRouteBlock, n4 - 1);  // unconditional loads
+      const int t = i / l4, j = 4 * (i - t * l4);
+      v[u] = load_act4<DT>(P.x, (size_t)t * P.H + k0 + j);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * kRouteBlock;
+      if (i < n4) {
+        const int t = i / l4, j = 4 * (i - t * l4);
+        *(float4*)(xsl + t * P.ks_len + j) = v[u];
+      }
+    }
+  }
+}
+
 // Grid (E/4, KS); wave w of block b handles expert 4b+w over values
-// [ks*ks_len, (ks+1)*ks_len) of the hidden dimension.
+// [ks*ks_len, (ks+1)*ks_len) of the hidden dimension (ks_len <= 1024, a
+// multiple of 256).  Loads are issued in batches before they are used.
 __global__ __launch_bounds__(kRouteBlock) void router_gemv_kernel(RouteParams P) {
   extern __shared__ __align__(16) float xsl[];  // [T][ks_len]
   const int ks = blockIdx.y;
   const int k0 = ks * P.ks_len;
   const int len = min(P.ks_len, P.H - k0);
-  for (int i = threadIdx.x; i < P.T * len; i += kRouteBlock) {
-    const int t = i / len, j = i - t * len;
-    xsl[t * P.ks_len + j] = load_act(P.x, P.x_dtype, (size_t)t * P.H + k0 + j);
-  }
+  if (P.x_dtype == QMOE_F32)
+    stage_x_slice<QMOE_F32>(P, k0, len, xsl);
+  else
+    stage_x_slice<QMOE_BF16>(P, k0, len, xsl);
   __syncthreads();
   const int lane = threadIdx.x & 63;
   const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (e >= P.E) return;
+  const float* wrow = P.Wr + (size_t)e * P.H + k0;
+  float4 w[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int j = 4 * lane + 256 * u;
+    w[u] = j < len ? *(const float4*)(wrow + j) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   float acc[kGemvRowsMax];
 #pragma unroll
-  for (int t = 0; t < kGemvRowsMax; ++t) acc[t] = 0.f;
-  const float* wrow = P.Wr + (size_t)e * P.H + k0;
-  for (int j = 4 * lane; j < len; j += 256) {
-    const float4 w = *(const float4*)(wrow + j);
+  for (int t = 0; t < kGemvRowsMax; ++t) {
+    acc[t] = 0.f;
+    if (t < P.T) {
 #pragma unroll
-    for (int t = 0; t < kGemvRowsMax; ++t) {
-      if (t < P.T) {
-        const float4 xv = *(const float4*)(xsl + t * P.ks_len + j);
-        acc[t] += w.x * xv.x + w.y * xv.y + w.z * xv.z + w.w * xv.w;
+      for (int u = 0; u < 4; ++u) {
+        const int j = 4 * lane + 256 * u;
+        if (j < len) {
+          const float4 xv = *(const float4*)(xsl + t * P.ks_len + j);
+          acc[t] += w[u].x * xv.x + w[u].y * xv.y + w[u].z * xv.z + w[u].w * xv.w;
+        }
       }
     }
   }
@@ -126,8 +170,17 @@ __global__ __launch_bounds__(kRouteBlock) void topk_kernel(RouteParams P) {
     const int e = lane + 64 * i;
     raw[i] = 0.f;
     if (e < P.E) {
+      // split-K partials in order, 8 loads in flight at a time
       float v = 0.f;
-      for (int s = 0; s < P.KS; ++s) v += P.part[((size_t)s * P.T + t) * P.E + e];
+      for (int s0 = 0; s0 < P.KS; s0 += 8) {
+        float pv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          pv[u] = s0 + u < P.KS ? P.part[((size_t)(s0 + u) * P.T + t) * P.E + e] : 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (s0 + u < P.KS) v += pv[u];
+      }
       if (P.bias) v += P.bias[e];
       raw[i] = v;
       if (P.logits) P.logits[(size_t)t * P.E + e] = v;

@@ -129,7 +129,11 @@ int qmoe_device_cu_count(void);
  * qgemv_<fmt>: y[r, n] = sum_k deq(W)[n, k] * x[r, k] for r < R, n < N
  *   ([P3] section 4.4 GEMV operator).  x is [R, K] of x_dtype, y is [R, N]
  *   fp32.  R >= 0 (R rows share one pass over W).  Activations are rounded to
- *   fp16 inside the dot product: |x| must stay below 65504.
+ *   fp16 inside the dot product: |x| must stay below 65504.  Up to 4 rows
+ *   (fewer for long K) run as fp16 dot products against the exact codes; more
+ *   rows, or K > 27456, run on the matrix cores, where each dequantized
+ *   weight is also rounded to fp16 (relative 2^-11; magnitudes below 2^-14
+ *   fall into fp16 subnormals).
  * Errors: INVALID_ARG for null pointers, N or K < 0, K % B != 0, K > 65536,
  *   misalignment; UNSUPPORTED for an unknown x_dtype.                      */
 #define QMOE_DECLARE_FORMAT(F)                                                 \
@@ -195,7 +199,10 @@ typedef struct qmoe_tier {
  * ([P2] bug item 4: gate, up and activation fused; [P3] 4.4: SwiGLU fused).
  * All tiers run in the same launches; rows o[pos] for pos >= offsets[E] are
  * not written.  offsets/perm are moe_permute's.  x as in moe_route; |x| and
- * |h| must stay below 65504 (fp16 inside the dot products).
+ * |h| must stay below 65504 (fp16 inside the dot products).  An expert with
+ * more rows than the dot-product blocking (1, 2 or 4 rows, set by T and by
+ * how many staged rows of length H or F fit in 64 KB of LDS) runs on the
+ * matrix cores with fp16-rounded weights, as in qgemv.
  * Limits: n_tiers <= QMOE_MAX_TIERS; H, F <= 65536.
  * Workspace: moe_ffn_workspace_size(T, k, F) bytes.                         */
 size_t moe_ffn_workspace_size(int T, int k, int F);

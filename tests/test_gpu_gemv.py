@@ -73,6 +73,20 @@ def test_gemv_within_bound(fmt, N, K, R):
     assert_within_bound(y, y_ref, bound, what=f"{fmt} {N}x{K} R={R}")
 
 
+@pytest.mark.parametrize("fmt", ["q6_k", "q4_0"])
+@pytest.mark.parametrize("R", [1, 2])
+def test_gemv_k_beyond_lds_staging(fmt, R):
+    """K = 28672 (a 70B-class FFN down projection): one activation row no
+    longer fits the LDS staging, so the matrix-core path serves every R."""
+    N, K = 40, 28672
+    W = synth.normal((N, K), 0.02, 6, synth.DENSE, K)
+    buf = fm.quantize(fmt, W)
+    x = synth.normal((R, K), 1.0, 6, synth.ACT, R)
+    y_ref, bound = moe.gemv(fmt, buf, N, K, x)
+    y = to_np(qmoe.gemv(fmt, to_gpu(buf), N, K, to_gpu(x)))
+    assert_within_bound(y, y_ref, bound, what=f"{fmt} K={K} R={R}")
+
+
 @pytest.mark.parametrize("fmt", ["q4_k", "q8_0"])
 def test_gemv_bf16_activations(fmt):
     N, K, R = 96, 7168, 16
