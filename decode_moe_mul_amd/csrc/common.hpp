@@ -180,6 +180,8 @@ QMOE_D void bytes_to_h2(const uint4 a, const uint4 b, uint32_t out[16]) {
 // (x & mask) | bits in one instruction.  The compiler splits this pattern
 // into an and plus an or when the operands are constants, so the operation
 // is written out; mask comes in a scalar register, bits in a vector one.
+// Only for values consumed by vector ALU instructions: the compiler does not
+// see this write when it spaces vector writes from matrix-core reads.
 QMOE_D uint32_t and_or(uint32_t x, uint32_t mask, uint32_t bits) {
   uint32_t r;
   asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(mask), "v"(bits));

@@ -133,40 +133,93 @@ struct Unit {
     coefs(u, c0, c1);
   }
 
-  // exact code values (bias removed) in nibble / byte order
-  QMOE_D void decode_exact(int u, uint32_t codes[16], float& c0, float& c1) const {
-    if constexpr (FMT == QMOE_Q8_0) bytes_to_h2(q, q2, codes);
-    else if constexpr (FMT == QMOE_Q4_0) nibbles_to_h2(q, H2_NEG_1032, codes);
-    else if constexpr (FMT == QMOE_MXFP4) e2m1_to_h2(q, codes);
-    else if constexpr (FMT == QMOE_Q4_K) nibbles_to_h2(q, H2_NEG_1024, codes);
-    else q6_to_h2(q, qh, codes);
+  // The 8-value slice [8g, 8g + 8) of unit u for the matrix-core path:
+  // q.x (Q8_0: q.x, q.y) holds its codes; scales as for the whole unit.
+  QMOE_D void load_slice(const Mat& M, int row, int u, int g, int K) {
+    const size_t nb32 = (size_t)(K >> 5);
+    if constexpr (FMT == QMOE_Q8_0) {
+      const uint2 v = *(const uint2*)(M.p0 + (size_t)row * K + 32 * (size_t)u + 8 * g);
+      q.x = v.x;
+      q.y = v.y;
+      s0 = ((const uint16_t*)M.p1)[row * nb32 + u];
+    } else {
+      q.x = *(const uint32_t*)(M.p0 + (size_t)row * (K >> 1) + 16 * (size_t)u + 4 * g);
+      if constexpr (FMT == QMOE_Q4_0) {
+        s0 = ((const uint16_t*)M.p1)[row * nb32 + u];
+      } else if constexpr (FMT == QMOE_MXFP4) {
+        s0 = M.p1[row * nb32 + u];
+      } else if constexpr (FMT == QMOE_Q4_K) {
+        meta = ((const uint4*)M.p1)[(size_t)row * (K >> 8) + (u >> 3)];
+      } else {
+        // high bits of values 8g..8g+7: bytes 2g, 2g + 1 of the unit's 8,
+        // read as the aligned word holding them (half picked at decode)
+        qh.x = *(const uint32_t*)(M.p1 + (size_t)row * (K >> 2) + 8 * (size_t)u + 4 * (g >> 1));
+        const size_t sb = (size_t)row * (K >> 8) + (u >> 3);
+        s0 = ((const uint32_t*)(M.p2 + 16 * sb))[(u & 7) >> 1];
+        s1 = ((const uint16_t*)M.p3)[sb];
+      }
+    }
+  }
+
+  // the slice as 4 fp16 pair words in slice order (slice_elem): exact codes,
+  // or biased ones (1024 + code, 1024 + 16 code on odd pairs) for Q4_0/Q4_K
+  QMOE_D void decode_slice(int u, int g, uint32_t out[4], float& c0, float& c1) const {
+    if constexpr (FMT == QMOE_Q8_0) {
+      const uint32_t w[2] = {q.x ^ 0x80808080u, q.y ^ 0x80808080u};
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        out[2 * i] = pk_add_h2(__builtin_amdgcn_perm(0x64646464u, w[i], 0x04020400u), H2_NEG_1152);
+        out[2 * i + 1] = pk_add_h2(__builtin_amdgcn_perm(0x64646464u, w[i], 0x04030401u), H2_NEG_1152);
+      }
+    } else if constexpr (FMT == QMOE_MXFP4) {
+      out[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q.x, 1.f, 0));
+      out[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q.x, 1.f, 1));
+      out[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q.x, 1.f, 2));
+      out[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q.x, 1.f, 3));
+    } else if constexpr (FMT == QMOE_Q6_K) {
+      const uint32_t h16 = (g & 1) ? qh.x >> 16 : qh.x & 0xFFFFu;
+      const uint32_t hh = (h16 & 0xFFu) | ((h16 & 0xFF00u) << 8);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const uint32_t lo = (q.x >> (4 * p)) & 0x000F000Fu;
+        const uint32_t hi = ((hh >> (2 * p)) & 0x00030003u) << 4;
+        out[p] = pk_add_h2(lo | hi | H2_MAGIC, H2_NEG_1056);
+      }
+    } else {
+      // plain and/or here, not the and_or helper: these words feed the
+      // matrix cores, and the compiler only inserts the wait states a
+      // vector write needs before a matrix-core read for code it generated
+      const uint32_t t = q.x >> 8;
+      out[0] = (q.x & 0x000F000Fu) | H2_MAGIC;
+      out[1] = (q.x & 0x00F000F0u) | H2_MAGIC;
+      out[2] = (t & 0x000F000Fu) | H2_MAGIC;
+      out[3] = (t & 0x00F000F0u) | H2_MAGIC;
+    }
     coefs(u, c0, c1);
   }
 };
 
-// acc[r] += <unit, activations of row r> for r < RC, from the biased codes;
-// bv[r] holds the unit's staged sums (see stage_rows).
-template <int FMT, int RC>
-QMOE_D void unit_dot(const uint32_t codes[16], float c0, float c1, const uint32_t (&xv)[RC][16],
-                     const float2 (&bv)[RC], float (&acc)[RC]) {
+// acc + <unit, one staged activation row>, from the biased codes; bv holds
+// the unit's staged sums for that row (see stage_rows).
+template <int FMT>
+QMOE_D float unit_dot(const uint32_t codes[16], float c0, float c1, const uint32_t xv[16],
+                      float2 bv, float acc) {
+  float s0 = 0.f, s1 = 0.f;
+  if constexpr (FMT == QMOE_Q6_K) {
 #pragma unroll
-  for (int r = 0; r < RC; ++r) {
-    float s0 = 0.f, s1 = 0.f;
-    if constexpr (FMT == QMOE_Q6_K) {
+    for (int p = 0; p < 8; ++p) s0 = fdot2(codes[p], xv[p], s0);
 #pragma unroll
-      for (int p = 0; p < 8; ++p) s0 = fdot2(codes[p], xv[r][p], s0);
+    for (int p = 8; p < 16; ++p) s1 = fdot2(codes[p], xv[p], s1);
+    return fmaf(c1, s1 - bv.y, fmaf(c0, s0 - bv.x, acc));
+  } else {
 #pragma unroll
-      for (int p = 8; p < 16; ++p) s1 = fdot2(codes[p], xv[r][p], s1);
-      acc[r] = fmaf(c1, s1 - bv[r].y, fmaf(c0, s0 - bv[r].x, acc[r]));
-    } else {
-#pragma unroll
-      for (int p = 0; p < 16; p += 2) {
-        s0 = fdot2(codes[p], xv[r][p], s0);
-        s1 = fdot2(codes[p + 1], xv[r][p + 1], s1);
-      }
-      acc[r] = fmaf(c0, (s0 + s1) - bv[r].x, acc[r]);
-      if constexpr (FMT == QMOE_Q4_K) acc[r] = fmaf(-c1, bv[r].y, acc[r]);
+    for (int p = 0; p < 16; p += 2) {
+      s0 = fdot2(codes[p], xv[p], s0);
+      s1 = fdot2(codes[p + 1], xv[p + 1], s1);
     }
+    acc = fmaf(c0, (s0 + s1) - bv.x, acc);
+    if constexpr (FMT == QMOE_Q4_K) acc = fmaf(-c1, bv.y, acc);
+    return acc;
   }
 }
 
@@ -291,30 +344,23 @@ QMOE_D void valu_pass(const Mat (&mats)[NMAT], int K, int rb, int re, int G, int
     if (++it == UPL) { it = 0; ++irg; }
   };
   auto compute = [&](Unit<FMT> (&w)[NMAT], int u, float (&acc)[NMAT][RC]) {
-    uint32_t xv[RC][16];
-    float2 bv[RC];
+    // decode every matrix's unit once, then take the staged rows one at a
+    // time (one row's activations live in registers at a time)
+    uint32_t codes[NMAT][16];
+    float c0[NMAT], c1[NMAT];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) w[m].decode(u, codes[m], c0[m], c1[m]);
 #pragma unroll
     for (int r = 0; r < RC; ++r) {
       if (r < rc) {
         const uint4* xp = (const uint4*)(xs + (size_t)r * ts + unit_off(u));
         const uint4 v0 = xp[0], v1 = xp[1], v2 = xp[2], v3 = xp[3];
-        xv[r][0] = v0.x; xv[r][1] = v0.y; xv[r][2] = v0.z; xv[r][3] = v0.w;
-        xv[r][4] = v1.x; xv[r][5] = v1.y; xv[r][6] = v1.z; xv[r][7] = v1.w;
-        xv[r][8] = v2.x; xv[r][9] = v2.y; xv[r][10] = v2.z; xv[r][11] = v2.w;
-        xv[r][12] = v3.x; xv[r][13] = v3.y; xv[r][14] = v3.z; xv[r][15] = v3.w;
-        bv[r] = FMT == QMOE_MXFP4 ? make_float2(0.f, 0.f) : sb[r * U + u];
-      } else {
+        const uint32_t xv[16] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w,
+                                 v2.x, v2.y, v2.z, v2.w, v3.x, v3.y, v3.z, v3.w};
+        const float2 bv = FMT == QMOE_MXFP4 ? make_float2(0.f, 0.f) : sb[r * U + u];
 #pragma unroll
-        for (int p = 0; p < 16; ++p) xv[r][p] = 0u;
-        bv[r] = make_float2(0.f, 0.f);
+        for (int m = 0; m < NMAT; ++m) acc[m][r] = unit_dot<FMT>(codes[m], c0[m], c1[m], xv, bv, acc[m][r]);
       }
-    }
-#pragma unroll
-    for (int m = 0; m < NMAT; ++m) {
-      uint32_t codes[16];
-      float c0, c1;
-      w[m].decode(u, codes, c0, c1);
-      unit_dot<FMT, RC>(codes, c0, c1, xv, bv, acc[m]);
     }
   };
 
@@ -401,172 +447,197 @@ QMOE_D void valu_rows(const Mat (&mats)[NMAT], int K, int rb, int re, int G, int
 // ------------------------------------------- many rows: matrix cores ----
 // Weight rows [cb, ce) of NMAT matrices [N, K] (the output columns) against
 // rows_total activation rows, in 16 x 16 output tiles on the matrix cores
-// (v_mfma_f32_16x16x32_f16, fp32 accumulation).  The 4 waves of the block
-// split K: wave w takes the 128-value quads w, w + 4, ... and the four
-// partial tiles are added in LDS in wave order.  Lane (n = lane % 16,
-// g = lane / 16) holds unit 4Q + g of weight row c + n and the same 32 values
-// of activation row n: the unit's exact fp16 codes (as on the dot-product
-// path) scaled in fp16, and the activations rounded to fp16, both listed in
-// the format's pair order, so the two operands agree on every K slot.  Loads
-// run one quad ahead of the matrix-core work.
+// (v_mfma_f32_16x16x32_f16, fp32 accumulation).  One matrix-core op covers
+// exactly one 32-value unit: lane (n = lane % 16, g = lane / 16) holds values
+// [8g, 8g + 8) of unit u of weight row c + n as exact fp16 codes and the same
+// values of activation row n rounded to fp16, so every product is exact and
+// the unit's scale is applied to the op's fp32 result (weights are never
+// rounded).  The 4-bit formats use biased codes (as on the dot-product path);
+// two more ops against constant operands give the unit's activation sums that
+// remove the bias and carry the Q4_K minimum.  Q6_K units have two 16-value
+// sub-scales, so they take two ops with half the lanes zeroed.  The 4 waves
+// split K (wave w takes units w, w + 4, ...) and add their partial tiles in
+// LDS in wave order; each slot's next unit is loaded as soon as the slot is
+// decoded, and the next unit's activations one unit ahead.
+// 16-column blocks per pass (gate and up together hold twice the registers)
+QMOE_HD constexpr int mfma_cols_per_pass(int nmat) { return nmat == 2 ? 2 : 4; }
 
-// 32 raw activation values (fp32: 8 x 16 B; bf16: the first 4 x 16 B),
-// converted only where they are used so the loads stay in flight.
-struct XRaw {
-  uint4 r[8];
+// Position within the 8-value slice of member i of pair p, and whether the
+// pair's codes sit four bits up (activations then divided by 16).
+template <int FMT>
+QMOE_HD int slice_elem(int p, int i) {
+  if constexpr (FMT == QMOE_Q8_0) return 4 * (p >> 1) + (p & 1) + 2 * i;
+  else if constexpr (FMT == QMOE_MXFP4) return 2 * p + i;
+  else return p + 4 * i;
+}
+template <int FMT>
+QMOE_HD bool slice_up4(int p) {
+  return (FMT == QMOE_Q4_0 || FMT == QMOE_Q4_K) && (p & 1);
+}
+template <int FMT>
+constexpr bool slice_biased() {
+  return FMT == QMOE_Q4_0 || FMT == QMOE_Q4_K;
+}
+
+// 8 raw activation values [8g, 8g + 8) of unit u (fp32: 32 B; bf16: 16 B)
+struct XRaw8 {
+  uint4 a, b;
 };
 
-QMOE_D void xraw_load(const void* row, int dtype, int u, XRaw& x) {
-  if (dtype == QMOE_F32) {
-    const uint4* p = (const uint4*)((const float*)row + 32 * u);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) x.r[i] = p[i];
+template <int XDT>
+QMOE_D void xslice_load(const void* row, int u, int g, XRaw8& x) {
+  if constexpr (XDT == QMOE_F32) {
+    const uint4* p = (const uint4*)((const float*)row + 32 * u + 8 * g);
+    x.a = p[0];
+    x.b = p[1];
   } else {
-    const uint4* p = (const uint4*)((const uint16_t*)row + 32 * u);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) x.r[i] = p[i];
+    x.a = *(const uint4*)((const uint16_t*)row + 32 * u + 8 * g);
   }
 }
 
-QMOE_D uint32_t word_of(const uint4& v, int i) {
-  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
-}
-
-// fp16 pairs of the 32 values in the pair order of format FMT
-template <int FMT>
-QMOE_D void xraw_pairs(const XRaw& x, int dtype, uint32_t out[16]) {
-  if (dtype == QMOE_F32) {
+// fp16 pair words of the slice in the format's slice order (zeros if !valid)
+template <int FMT, int XDT>
+QMOE_D void xslice_pairs(const XRaw8& x, bool valid, uint32_t out[4]) {
+  float v[8];
+  if constexpr (XDT == QMOE_F32) {
+    const uint32_t w[8] = {x.a.x, x.a.y, x.a.z, x.a.w, x.b.x, x.b.y, x.b.z, x.b.w};
 #pragma unroll
-    for (int p = 0; p < 16; ++p) {
-      const int e0 = byte_order(FMT) ? pair_elem_byte(p, 0) : pair_elem_nibble(p, 0);
-      const int e1 = byte_order(FMT) ? pair_elem_byte(p, 1) : pair_elem_nibble(p, 1);
-      out[p] = pack_f16(__builtin_bit_cast(float, word_of(x.r[e0 >> 2], e0 & 3)),
-                        __builtin_bit_cast(float, word_of(x.r[e1 >> 2], e1 & 3)));
-    }
+    for (int i = 0; i < 8; ++i) v[i] = __builtin_bit_cast(float, w[i]);
   } else {
+    const uint32_t w[4] = {x.a.x, x.a.y, x.a.z, x.a.w};
 #pragma unroll
-    for (int p = 0; p < 16; ++p) {
-      const int e0 = byte_order(FMT) ? pair_elem_byte(p, 0) : pair_elem_nibble(p, 0);
-      const int e1 = byte_order(FMT) ? pair_elem_byte(p, 1) : pair_elem_nibble(p, 1);
-      const uint32_t w0 = word_of(x.r[e0 >> 3], (e0 >> 1) & 3);
-      const uint32_t w1 = word_of(x.r[e1 >> 3], (e1 >> 1) & 3);
-      out[p] = pack_f16(bf16_bits_to_f32((e0 & 1) ? w0 >> 16 : w0 & 0xFFFFu),
-                        bf16_bits_to_f32((e1 & 1) ? w1 >> 16 : w1 & 0xFFFFu));
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16_bits_to_f32(w[i] & 0xFFFFu);
+      v[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
     }
   }
-}
-
-// Unit values in fp16: codes times the unit coefficients (minus the Q4_K
-// offset), one packed fp16 operation per pair.
-template <int FMT>
-QMOE_D void scale_codes(const uint32_t codes[16], float c0, float c1, uint32_t out[16]) {
-  if constexpr (FMT == QMOE_Q4_K) {
-    const h2_t a = __builtin_bit_cast(h2_t, pack_f16(c0, c0));
-    const h2_t b = __builtin_bit_cast(h2_t, pack_f16(-c1, -c1));
 #pragma unroll
-    for (int p = 0; p < 16; ++p)
-      out[p] = __builtin_bit_cast(uint32_t,
-                                  __builtin_elementwise_fma(__builtin_bit_cast(h2_t, codes[p]), a, b));
-  } else if constexpr (FMT == QMOE_Q6_K) {
-    const uint32_t a = pack_f16(c0, c0), b = pack_f16(c1, c1);
-#pragma unroll
-    for (int p = 0; p < 16; ++p) out[p] = pk_mul_h2(codes[p], p < 8 ? a : b);
-  } else {
-    const uint32_t a = pack_f16(c0, c0);
-#pragma unroll
-    for (int p = 0; p < 16; ++p) out[p] = pk_mul_h2(codes[p], a);
+  for (int p = 0; p < 4; ++p) {
+    uint32_t h = pack_f16(v[slice_elem<FMT>(p, 0)], v[slice_elem<FMT>(p, 1)]);
+    if (slice_up4<FMT>(p)) h = pk_mul_h2(h, 0x2C002C00u);  // x 1/16, exact
+    out[p] = valid ? h : 0u;
   }
 }
 
-QMOE_HD size_t mfma_red_bytes(int nmat) { return (size_t)kWaves * nmat * 4 * 64 * sizeof(float); }
+QMOE_D f32x4_t mfma16(const uint32_t a[4], const uint32_t b[4], f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(
+      __builtin_bit_cast(f16x8_t, make_uint4(a[0], a[1], a[2], a[3])),
+      __builtin_bit_cast(f16x8_t, make_uint4(b[0], b[1], b[2], b[3])), c, 0, 0, 0);
+}
 
-template <int FMT, int NMAT, class SrcOf, class SinkOf>
-QMOE_D void mfma_cols(const Mat (&mats)[NMAT], int K, int cb, int ce, int rows_total, int dtype,
+QMOE_HD size_t mfma_red_bytes(int nmat) {
+  return (size_t)kWaves * mfma_cols_per_pass(nmat) * nmat * 4 * 64 * sizeof(float);
+}
+
+template <int FMT, int NMAT, int XDT, class SrcOf, class SinkOf>
+QMOE_D void mfma_cols(const Mat (&mats)[NMAT], int K, int cb, int ce, int rows_total,
                       uint8_t* lds, SrcOf src_of, SinkOf sink_of) {
+  constexpr int NC = mfma_cols_per_pass(NMAT);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
-  const int U = K >> 5, nquad = (U + 3) >> 2;
-  float* red = (float*)lds;  // [kWaves][NMAT][4][64]
-  __syncthreads();           // earlier readers of the LDS are done
-  for (int c = cb; c < ce; c += 16) {
-    const int col = c + n;
-    const bool cvalid = col < ce;
-    for (int c0 = 0; c0 < rows_total; c0 += 16) {
-      const int ar = c0 + n;
-      const bool rvalid = ar < rows_total;
-      const void* xrow = src_of(rvalid ? ar : 0);
-      f32x4_t acc[NMAT];
+  const int U = K >> 5;
+  const int nu = U > wave ? (U - wave + kWaves - 1) / kWaves : 0;  // this wave's units
+  float* red = (float*)lds;  // [kWaves][NC][NMAT][4][64]
+  const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+  __syncthreads();  // earlier readers of the LDS are done
+  for (int r0 = 0; r0 < rows_total; r0 += 16) {
+    const bool rvalid = r0 + n < rows_total;
+    const void* xrow = src_of(rvalid ? r0 + n : r0);
+    for (int cg = cb; cg < ce; cg += 16 * NC) {
+      f32x4_t acc[NC][NMAT];
 #pragma unroll
-      for (int m = 0; m < NMAT; ++m) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      // One load buffer per operand: each is decoded into operand registers
-      // and at once refilled with the wave's next quad, so the matrix-core
-      // work runs while those loads are in flight.
-      Unit<FMT> w[NMAT];
-      XRaw x;
-      auto fetch_x = [&](int Q) {
-        const int u = 4 * Q + g;
-        if (u < U && rvalid) {
-          xraw_load(xrow, dtype, u, x);
-        } else {
+      for (int c = 0; c < NC; ++c)
 #pragma unroll
-          for (int i = 0; i < 8; ++i) x.r[i] = make_uint4(0u, 0u, 0u, 0u);
-        }
-      };
-      if (wave < nquad) {
-        fetch_x(wave);
-        if (4 * wave + g < U && cvalid) {
+        for (int m = 0; m < NMAT; ++m) acc[c][m] = zero;
+      if (nu > 0) {
+        // loads are unconditional: rows past ce re-read row ce - 1 and units
+        // past the wave's last re-read it (their results are not used)
+        auto unit_of = [&](int ui) { return wave + kWaves * min(ui, nu - 1); };
+        int wrow[NC];
 #pragma unroll
-          for (int m = 0; m < NMAT; ++m) w[m].load(mats[m], col, 4 * wave + g, K);
+        for (int c = 0; c < NC; ++c) wrow[c] = min(cg + 16 * c + n, ce - 1);
+        Unit<FMT> w[NC][NMAT];
+        XRaw8 xr;
+        xslice_load<XDT>(xrow, unit_of(0), g, xr);
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+          for (int m = 0; m < NMAT; ++m) w[c][m].load_slice(mats[m], wrow[c], unit_of(0), g, K);
+        for (int ui = 0; ui < nu; ++ui) {
+          const int u = unit_of(ui), un = unit_of(ui + 1);
+          uint32_t xa[4];
+          xslice_pairs<FMT, XDT>(xr, rvalid, xa);
+          xslice_load<XDT>(xrow, un, g, xr);
+          f32x4_t s_st = zero, s_x = zero;  // sums of staged / effective activations
+          if constexpr (slice_biased<FMT>()) {
+            const uint32_t ones[4] = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
+            const uint32_t eff[4] = {0x3C003C00u, 0x4C004C00u, 0x3C003C00u, 0x4C004C00u};
+            s_st = mfma16(xa, ones, zero);
+            s_x = mfma16(xa, eff, zero);
+          }
+#pragma unroll
+          for (int c = 0; c < NC; ++c) {
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m) {
+              uint32_t bw[4];
+              float c0, c1;
+              w[c][m].decode_slice(u, g, bw, c0, c1);
+              w[c][m].load_slice(mats[m], wrow[c], un, g, K);
+              if constexpr (FMT == QMOE_Q6_K) {
+                uint32_t lo[4], hi[4];
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                  lo[p] = g < 2 ? bw[p] : 0u;
+                  hi[p] = g < 2 ? 0u : bw[p];
+                }
+                const f32x4_t dl = mfma16(xa, lo, zero), dh = mfma16(xa, hi, zero);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                  acc[c][m][j] = fmaf(c1, dh[j], fmaf(c0, dl[j], acc[c][m][j]));
+              } else {
+                const f32x4_t d = mfma16(xa, bw, zero);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                  if constexpr (FMT == QMOE_Q4_K) {
+                    acc[c][m][j] = fmaf(-c1, s_x[j], fmaf(c0, d[j] - 1024.f * s_st[j], acc[c][m][j]));
+                  } else if constexpr (FMT == QMOE_Q4_0) {
+                    acc[c][m][j] = fmaf(c0, d[j] - (1024.f * s_st[j] + 8.f * s_x[j]), acc[c][m][j]);
+                  } else {
+                    acc[c][m][j] = fmaf(c0, d[j], acc[c][m][j]);
+                  }
+                }
+              }
+            }
+          }
         }
       }
-      for (int Q = wave; Q < nquad; Q += kWaves) {
-        const int u = 4 * Q + g, un = u + 4 * kWaves;
-        const bool more = Q + kWaves < nquad;
-        uint32_t xv[16];
-        xraw_pairs<FMT>(x, dtype, xv);
-        if (more) fetch_x(Q + kWaves);
+      // lane holds activation rows r0 + 4g + j of weight row cg + 16c + n;
+      // wave j adds the four waves' partials for row 4g + j in wave order
 #pragma unroll
-        for (int m = 0; m < NMAT; ++m) {
-          uint32_t wv[16];
-          if (u < U && cvalid) {
-            uint32_t codes[16];
-            float s0, s1;
-            w[m].decode_exact(u, codes, s0, s1);
-            scale_codes<FMT>(codes, s0, s1, wv);
-          } else {
+      for (int c = 0; c < NC; ++c)
 #pragma unroll
-            for (int p = 0; p < 16; ++p) wv[p] = 0u;
-          }
-          if (more && un < U && cvalid) w[m].load(mats[m], col, un, K);
+        for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint4 a = make_uint4(xv[4 * q], xv[4 * q + 1], xv[4 * q + 2], xv[4 * q + 3]);
-            const uint4 b = make_uint4(wv[4 * q], wv[4 * q + 1], wv[4 * q + 2], wv[4 * q + 3]);
-            acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
-                                                            __builtin_bit_cast(f16x8_t, b),
-                                                            acc[m], 0, 0, 0);
-          }
-        }
-      }
-      // lane holds activation rows c0 + 4g + j (j < 4) of weight row col
-#pragma unroll
-      for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) red[((wave * NMAT + m) * 4 + j) * 64 + lane] = acc[m][j];
+          for (int j = 0; j < 4; ++j)
+            red[(((wave * NC + c) * NMAT + m) * 4 + j) * 64 + lane] = acc[c][m][j];
       __syncthreads();
       {
-        const int j = wave;  // wave j finishes row 4g + j of every lane's tile
-        const int r = c0 + 4 * g + j;
-        if (cvalid && r < rows_total) {
-          float v[NMAT];
+        const int j = wave, r = r0 + 4 * g + j;
 #pragma unroll
-          for (int m = 0; m < NMAT; ++m) {
-            float sum = red[((0 * NMAT + m) * 4 + j) * 64 + lane];
+        for (int c = 0; c < NC; ++c) {
+          const int col = cg + 16 * c + n;
+          if (col < ce && r < rows_total) {
+            float v[NMAT];
 #pragma unroll
-            for (int w = 1; w < kWaves; ++w) sum += red[((w * NMAT + m) * 4 + j) * 64 + lane];
-            v[m] = sum;
+            for (int m = 0; m < NMAT; ++m) {
+              float sum = red[(((0 * NC + c) * NMAT + m) * 4 + j) * 64 + lane];
+#pragma unroll
+              for (int w = 1; w < kWaves; ++w)
+                sum += red[(((w * NC + c) * NMAT + m) * 4 + j) * 64 + lane];
+              v[m] = sum;
+            }
+            sink_of(col, r, v);
           }
-          sink_of(col, r, v);
         }
       }
       __syncthreads();
@@ -595,8 +666,12 @@ __global__ __launch_bounds__(kBlock) void qgemv_kernel(GemvParams P) {
   const size_t xrow_bytes = (size_t)K * (dtype == QMOE_F32 ? 4 : 2);
   auto src = [=](int r) { return (const void*)(xb + (size_t)r * xrow_bytes); };
   auto sink = [=](int n, int r, const float* a) { y[(size_t)r * N + n] = a[0]; };
-  if (MFMA)
-    mfma_cols<FMT, 1>(mats, K, rb, re, P.R, dtype, smem, src, sink);
+  if (MFMA) {
+    if (dtype == QMOE_F32)
+      mfma_cols<FMT, 1, QMOE_F32>(mats, K, rb, re, P.R, smem, src, sink);
+    else
+      mfma_cols<FMT, 1, QMOE_BF16>(mats, K, rb, re, P.R, smem, src, sink);
+  }
   else
     valu_rows<FMT, 1, RC>(mats, K, rb, re, P.G, P.R, dtype, smem, src, sink);
 }
@@ -699,7 +774,7 @@ QMOE_D int scheduled_expert(const int* offs, int E, int m_max, int b, int ntiles
 // experts with more than m_max rows can occur (the matrix-core branch costs
 // registers, so launches that cannot use it leave it out).
 template <int PHASE, int RC, bool MFMA>
-__global__ __launch_bounds__(kBlock) void ffn_decode_kernel(FfnParams P) {
+__global__ __launch_bounds__(kBlock, 2) void ffn_decode_kernel(FfnParams P) {
   extern __shared__ __align__(16) uint8_t smem[];
   // scalars used below, read once from the argument block
   const int E = P.E, H = P.H, F = P.F, kk = P.k, dtype = P.x_dtype, m_max = P.m_max;
@@ -722,8 +797,10 @@ __global__ __launch_bounds__(kBlock) void ffn_decode_kernel(FfnParams P) {
   const int fmt = PHASE == 0 ? t.fmt_gate_up : t.fmt_down;
   const int N = PHASE == 0 ? F : H, K = PHASE == 0 ? H : F;
   // few-row experts: weight rows [rb, re) of a row tile; many-row experts:
-  // a 16-aligned column slice, N split over ntiles_big blocks
-  const int cpt = ((N + P.ntiles_big - 1) / P.ntiles_big + 15) / 16 * 16;
+  // a slice of whole matrix-core passes, N split over at most
+  // ntiles_big blocks
+  const int pass = 16 * mfma_cols_per_pass(PHASE == 0 ? 2 : 1);
+  const int cpt = ((N + P.ntiles_big - 1) / P.ntiles_big + pass - 1) / pass * pass;
   const int rb = big ? tile * cpt : tile * tile_rows;
   const int re = min(N, rb + (big ? cpt : tile_rows));
   if (rb >= re) return;
@@ -742,11 +819,14 @@ __global__ __launch_bounds__(kBlock) void ffn_decode_kernel(FfnParams P) {
     if (PHASE == 0) {                                                                      \
       const Mat mats[2] = {mat_of((const uint8_t*)t.gate + eo, FM, N, K),                  \
                            mat_of((const uint8_t*)t.up + eo, FM, N, K)};                   \
-      if (MFMA && big) mfma_cols<FM, 2>(mats, K, rb, re, m, dtype, smem, x_row, h_out);             \
+      if (MFMA && big && dtype == QMOE_F32)                                                \
+        mfma_cols<FM, 2, QMOE_F32>(mats, K, rb, re, m, smem, x_row, h_out);                \
+      else if (MFMA && big)                                                                \
+        mfma_cols<FM, 2, QMOE_BF16>(mats, K, rb, re, m, smem, x_row, h_out);               \
       else valu_rows<FM, 2, RC>(mats, K, rb, re, G, m, dtype, smem, x_row, h_out);         \
     } else {                                                                               \
       const Mat mats[1] = {mat_of((const uint8_t*)t.down + eo, FM, N, K)};                 \
-      if (MFMA && big) mfma_cols<FM, 1>(mats, K, rb, re, m, QMOE_F32, smem, h_row, o_out);         \
+      if (MFMA && big) mfma_cols<FM, 1, QMOE_F32>(mats, K, rb, re, m, smem, h_row, o_out);         \
       else valu_rows<FM, 1, RC>(mats, K, rb, re, G, m, QMOE_F32, smem, h_row, o_out);      \
     }                                                                                      \
   } break;
@@ -825,6 +905,10 @@ static int qgemv_launch(int FMT, const void* W, int N, int K, const void* x, int
   const int RC = pick_rc(R, K);
   GemvParams P{W, N, K, x, x_dtype, R, y, lanes_per_row(K), 0};
   P.tile_rows = pick_tile_rows(N, P.G, 1);
+  if (R > RC) {  // matrix-core tiles: whole 64-column passes
+    const int pass = 16 * mfma_cols_per_pass(1);
+    P.tile_rows = (P.tile_rows + pass - 1) / pass * pass;
+  }
   const dim3 grid((N + P.tile_rows - 1) / P.tile_rows);
   const size_t lds = R > RC ? mfma_red_bytes(1) : stage_bytes(RC, K);
   hipStream_t s = (hipStream_t)stream;

@@ -99,6 +99,18 @@ def test_small_shared_bf16_layer():
     _check_layer(SMALL_SHARED, 16)
 
 
+WIDE_HIDDEN = MoEConfig("wide_hidden", H=28672, E=4, k=2, F=64,
+                        tiers=(Tier(0, 2, "q6_k", "q8_0"), Tier(2, 4, "q4_k", "q4_0")),
+                        rows=(3,))
+
+
+@pytest.mark.parametrize("T", [1, 3])
+def test_hidden_too_wide_for_lds_staging(T):
+    """A 28672-wide hidden row does not fit the LDS staging of the dot-product
+    path; the gate/up phase then runs every expert on the matrix cores."""
+    _check_layer(WIDE_HIDDEN, T)
+
+
 @pytest.mark.parametrize("T", [1, 6])
 def test_tiered_layer_full_size(T):
     """512 experts, top-10, hidden 2048, FFN 640, three tiers, rank prior."""
