@@ -556,18 +556,24 @@ QMOE_D void mfma_cols(const Mat (&mats)[NMAT], int K, int cb, int ce, int rows_t
         int wrow[NC];
 #pragma unroll
         for (int c = 0; c < NC; ++c) wrow[c] = min(cg + 16 * c + n, ce - 1);
-        Unit<FMT> w[NC][NMAT];
-        XRaw8 xr;
-        xslice_load<XDT>(xrow, unit_of(0), g, xr);
+        // two slot sets, each holding one unit's slices, consumed in turn
+        // and refilled with the unit two ahead: two units of loads are in
+        // flight while one is computed
+        Unit<FMT> wa[NC][NMAT], wb[NC][NMAT];
+        XRaw8 xa_raw, xb_raw;
+        auto fill = [&](Unit<FMT> (&w)[NC][NMAT], XRaw8& xr, int ui) {
+          const int u = unit_of(ui);
+          xslice_load<XDT>(xrow, u, g, xr);
 #pragma unroll
-        for (int c = 0; c < NC; ++c)
+          for (int c = 0; c < NC; ++c)
 #pragma unroll
-          for (int m = 0; m < NMAT; ++m) w[c][m].load_slice(mats[m], wrow[c], unit_of(0), g, K);
-        for (int ui = 0; ui < nu; ++ui) {
-          const int u = unit_of(ui), un = unit_of(ui + 1);
+            for (int m = 0; m < NMAT; ++m) w[c][m].load_slice(mats[m], wrow[c], u, g, K);
+        };
+        // keep = 0 for the unit past the wave's last (its slices are a re-read)
+        auto step = [&](Unit<FMT> (&w)[NC][NMAT], XRaw8& xr, int ui, float keep) {
+          const int u = unit_of(ui);
           uint32_t xa[4];
           xslice_pairs<FMT, XDT>(xr, rvalid, xa);
-          xslice_load<XDT>(xrow, un, g, xr);
           f32x4_t s_st = zero, s_x = zero;  // sums of staged / effective activations
           if constexpr (slice_biased<FMT>()) {
             const uint32_t ones[4] = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
@@ -575,40 +581,67 @@ QMOE_D void mfma_cols(const Mat (&mats)[NMAT], int K, int cb, int ce, int rows_t
             s_st = mfma16(xa, ones, zero);
             s_x = mfma16(xa, eff, zero);
           }
+          uint32_t bw[NC][NMAT][4];
+          float c0[NC][NMAT], c1[NC][NMAT];
+#pragma unroll
+          for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m) {
+              w[c][m].decode_slice(u, g, bw[c][m], c0[c][m], c1[c][m]);
+              c0[c][m] *= keep;
+              c1[c][m] *= keep;
+              // the decoded operands are materialised here (an empty volatile
+              // asm the compiler cannot move or see through), so no part of
+              // the decode sinks below the refill and the loaded words need
+              // not outlive it
+              asm volatile("" : "+v"(c0[c][m]), "+v"(c1[c][m]), "+v"(bw[c][m][0]),
+                           "+v"(bw[c][m][1]), "+v"(bw[c][m][2]), "+v"(bw[c][m][3]));
+            }
+          // the barriers keep each set's refill in program order, so the wait
+          // for a set leaves the other set's loads in flight
+          __builtin_amdgcn_sched_barrier(0);
+          fill(w, xr, ui + 2);
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int c = 0; c < NC; ++c) {
 #pragma unroll
             for (int m = 0; m < NMAT; ++m) {
-              uint32_t bw[4];
-              float c0, c1;
-              w[c][m].decode_slice(u, g, bw, c0, c1);
-              w[c][m].load_slice(mats[m], wrow[c], un, g, K);
               if constexpr (FMT == QMOE_Q6_K) {
                 uint32_t lo[4], hi[4];
 #pragma unroll
                 for (int p = 0; p < 4; ++p) {
-                  lo[p] = g < 2 ? bw[p] : 0u;
-                  hi[p] = g < 2 ? 0u : bw[p];
+                  lo[p] = g < 2 ? bw[c][m][p] : 0u;
+                  hi[p] = g < 2 ? 0u : bw[c][m][p];
                 }
                 const f32x4_t dl = mfma16(xa, lo, zero), dh = mfma16(xa, hi, zero);
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                  acc[c][m][j] = fmaf(c1, dh[j], fmaf(c0, dl[j], acc[c][m][j]));
+                  acc[c][m][j] = fmaf(c1[c][m], dh[j], fmaf(c0[c][m], dl[j], acc[c][m][j]));
               } else {
-                const f32x4_t d = mfma16(xa, bw, zero);
+                const f32x4_t d = mfma16(xa, bw[c][m], zero);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                   if constexpr (FMT == QMOE_Q4_K) {
-                    acc[c][m][j] = fmaf(-c1, s_x[j], fmaf(c0, d[j] - 1024.f * s_st[j], acc[c][m][j]));
+                    acc[c][m][j] = fmaf(-c1[c][m], s_x[j],
+                                        fmaf(c0[c][m], d[j] - 1024.f * s_st[j], acc[c][m][j]));
                   } else if constexpr (FMT == QMOE_Q4_0) {
-                    acc[c][m][j] = fmaf(c0, d[j] - (1024.f * s_st[j] + 8.f * s_x[j]), acc[c][m][j]);
+                    acc[c][m][j] =
+                        fmaf(c0[c][m], d[j] - (1024.f * s_st[j] + 8.f * s_x[j]), acc[c][m][j]);
                   } else {
-                    acc[c][m][j] = fmaf(c0, d[j], acc[c][m][j]);
+                    acc[c][m][j] = fmaf(c0[c][m], d[j], acc[c][m][j]);
                   }
                 }
               }
             }
           }
+        };
+        fill(wa, xa_raw, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        fill(wb, xb_raw, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        for (int ui = 0; ui < nu; ui += 2) {
+          step(wa, xa_raw, ui, 1.f);
+          step(wb, xb_raw, ui + 1, ui + 1 < nu ? 1.f : 0.f);
         }
       }
       // lane holds activation rows r0 + 4g + j of weight row cg + 16c + n;
