@@ -16,9 +16,16 @@ rows so the expert set changes from call to call.
 value = weight bytes streamed per step (router + each distinct selected
 expert, shared included) / wall time per step, in GB/s.
 
-Extra fields: tokens/s per row count, fraction of the 8 TB/s HBM peak, the
-roofline of the dominant kernel (ffn_gate_up) from per-launch HIP events
-inside the timed region, and the CPU oracle timed on a bounded sample.
+Timed passes (each over the same steps, inputs and weight rotation):
+  1. the step itself, with HIP events only before and after: value,
+     ms_per_step (nothing is recorded between kernels, since every event
+     record between dependent kernels lengthens the gap between them);
+  2. each row count alone: tokens_per_s, ms_per_call;
+  3. the library's HIP events around every gate/up launch only: the
+     roofline of the dominant kernel (ffn_gate_up);
+  4. events around every launch: kernel_ms_per_step (context only).
+Also reported: the fraction of the 8 TB/s HBM peak, the gate/up HBM traffic
+from stored counter runs, and the CPU oracle timed on a bounded sample.
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--no-cpu-baseline]
 """
@@ -242,28 +249,41 @@ def main():
             layer.forward(x, copy)
     torch.cuda.synchronize()
 
-    # timed region: per-call events (for tokens/s per row count) and the
-    # library's per-launch events (for the dominant kernel's roofline)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(a.steps)]
+    def timed(calls_of_step, tag):
+        """ms for a.steps steps of the given calls, events only at the ends."""
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for s in range(a.steps):
+            for layer, x, copy, rows in calls_of_step(s):
+                layer.forward(x, copy)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        log(f"timed {tag}: {t0.elapsed_time(t1) / a.steps:.4f} ms per step")
+        return t0.elapsed_time(t1)
+
+    # 1. the step (value, ms_per_step): the three calls, nothing recorded
+    #    between kernels
+    total_ms = timed(lambda s: step_calls(tiered, grouped, xt, xg, s), "step")
+    ms_step = total_ms / a.steps
+    # 2. each row count on its own, same inputs and weight rotation
+    call_ms = np.array([timed(lambda s, i=i: [step_calls(tiered, grouped, xt, xg, s)[i]],
+                              f"rows={r}") for i, r in enumerate((1, 6, 16))])
+    # 3. the dominant kernel: library HIP events around every gate/up launch
+    #    (recorded on the launch stream) over the same steps
+    qmoe.profile_reset()
+    qmoe.profile_only("ffn_gate_up")
+    qmoe.profile_enable(True)
+    timed(lambda s: step_calls(tiered, grouped, xt, xg, s), "gate/up events")
+    qmoe.profile_enable(False)
+    qmoe.profile_only(None)
+    n_gu, gu_ms = qmoe.profile_read("ffn_gate_up")
+    # 4. every kernel's time (events around all launches; reported only)
     qmoe.profile_reset()
     qmoe.profile_enable(True)
-    torch.cuda.synchronize()
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    t_start.record(stream)
-    for s in range(a.steps):
-        ev[s][0].record(stream)
-        for i, (layer, x, copy, rows) in enumerate(step_calls(tiered, grouped, xt, xg, s)):
-            layer.forward(x, copy)
-            ev[s][i + 1].record(stream)
-    t_end.record(stream)
-    torch.cuda.synchronize()
+    timed(lambda s: step_calls(tiered, grouped, xt, xg, s), "all-kernel events")
     qmoe.profile_enable(False)
-    total_ms = t_start.elapsed_time(t_end)
-    ms_step = total_ms / a.steps
-    call_ms = np.array([[ev[s][i].elapsed_time(ev[s][i + 1]) for i in range(3)]
-                        for s in range(a.steps)]).sum(axis=0)
-    n_gu, gu_ms = qmoe.profile_read("ffn_gate_up")
     kernel_ms = {k: qmoe.profile_read(k) for k in
                  ("router_gemv", "topk", "permute", "ffn_gate_up", "ffn_down", "combine")}
 

@@ -54,6 +54,7 @@ static bool g_prof_on = false;
 static std::vector<Record> g_records;
 static std::vector<hipEvent_t> g_event_pool;
 static Record* g_open = nullptr;
+static std::string g_prof_only;  // record only this kernel name when not empty
 
 static hipEvent_t take_event() {
   if (!g_event_pool.empty()) {
@@ -70,6 +71,8 @@ bool profiling_on() { return g_prof_on; }
 
 void profile_begin(const char* kernel, hipStream_t s) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_open = nullptr;
+  if (!g_prof_only.empty() && g_prof_only != kernel) return;
   Record r{kernel, take_event(), take_event()};
   if (!r.start || !r.stop) return;
   hipEventRecord(r.start, s);
@@ -159,6 +162,12 @@ int qmoe_device_cu_count(void) { return cu_count(); }
 int qmoe_profile_enable(int on) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
   g_prof_on = on != 0;
+  return QMOE_OK;
+}
+
+int qmoe_profile_only(const char* name) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_only = name ? name : "";
   return QMOE_OK;
 }
 

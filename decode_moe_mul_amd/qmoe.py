@@ -51,6 +51,7 @@ _SIGNATURES = {
     "moe_combine": (_I, [_VP, _VP, _VP, _I, _I, _I, _VP, _VP, _VP]),
     "qmoe_profile_enable": (_I, [_I]),
     "qmoe_profile_reset": (_I, []),
+    "qmoe_profile_only": (_I, [ctypes.c_char_p]),
     "qmoe_profile_read": (_I, [ctypes.c_char_p, ctypes.POINTER(_I),
                                ctypes.POINTER(ctypes.c_double)]),
 }
@@ -284,6 +285,11 @@ def combine(o, inv_perm, p, T, k, H, shared=None, out=None):
 
 def profile_enable(on=True):
     _check(lib().qmoe_profile_enable(1 if on else 0), "qmoe_profile_enable")
+
+
+def profile_only(name=None):
+    """Record only launches of kernel `name` (None: all)."""
+    _check(lib().qmoe_profile_only(None if name is None else name.encode()), "qmoe_profile_only")
 
 
 def profile_reset():

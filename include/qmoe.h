@@ -236,8 +236,12 @@ int moe_combine(const float *o, const int32_t *inv_perm, const float *p, int T,
  * Optional per-kernel timing with HIP events recorded around every launch the
  * library makes while enabled (on the launch stream).  qmoe_profile_read
  * waits for the recorded events and returns, for the kernel named `name`,
- * the number of launches and their summed duration in milliseconds.         */
+ * the number of launches and their summed duration in milliseconds.
+ * qmoe_profile_only(name) restricts recording to launches of that kernel
+ * (NULL: all kernels); each recorded launch adds two event records to its
+ * stream, so timing one kernel perturbs the others least.                   */
 int qmoe_profile_enable(int on);
+int qmoe_profile_only(const char *name);
 int qmoe_profile_reset(void);
 int qmoe_profile_read(const char *name, int *launches, double *total_ms);
 
