@@ -1,8 +1,8 @@
 """Benchmark: routed-expert (MoE) quantized decode on one MI355X.
 
-One step = one pass of the whole decode path (moe_route -> moe_permute ->
-moe_ffn_tiered -> moe_combine) over three layer calls, the decode row counts
-the metric names:
+One step = one pass of the whole decode path (moe_route_decode, which is
+moe_route + moe_permute in one launch -> moe_ffn_tiered -> moe_combine) over
+three layer calls, the decode row counts the metric names:
   * 1 row and 6 rows through the tiered 512-expert top-10 layer (hidden 2048,
     FFN 640; Q6_K/Q8_0 hot, Q4_K/Q4_0 middle, MXFP4 tail; rank prior),
   * 16 bf16 rows through the grouped 256-expert top-8 layer (hidden 7168,
@@ -285,7 +285,8 @@ def main():
     timed(lambda s: step_calls(tiered, grouped, xt, xg, s), "all-kernel events")
     qmoe.profile_enable(False)
     kernel_ms = {k: qmoe.profile_read(k) for k in
-                 ("router_gemv", "topk", "permute", "ffn_gate_up", "ffn_down", "combine")}
+                 ("route_decode", "router_gemv", "topk", "permute", "ffn_gate_up", "ffn_down",
+                  "combine")}
 
     t = stored_traffic()
     traffic = None if t is None else int(t["traffic_bytes_per_launch"])

@@ -262,6 +262,34 @@ QMOE_HD bool pair_up4(int p) {
 }
 
 // ------------------------------------------------- wave reductions ------
+// Wave-wide max / min of unsigned values through DPP row shifts and row
+// broadcasts (lanes whose source is out of range keep the identity); the
+// result is read from lane 63 and is wave-uniform.
+template <int CTRL, int ROW_MASK>
+QMOE_D uint32_t dpp_u32(uint32_t identity, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)identity, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+QMOE_D uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<0x111, 0xF>(0u, v));  // row_shr:1
+  v = max(v, dpp_u32<0x112, 0xF>(0u, v));  // row_shr:2
+  v = max(v, dpp_u32<0x114, 0xF>(0u, v));  // row_shr:4
+  v = max(v, dpp_u32<0x118, 0xF>(0u, v));  // row_shr:8
+  v = max(v, dpp_u32<0x142, 0xA>(0u, v));  // row_bcast:15
+  v = max(v, dpp_u32<0x143, 0xC>(0u, v));  // row_bcast:31
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+QMOE_D uint32_t wave_min_u32(uint32_t v) {
+  const uint32_t id = 0xFFFFFFFFu;
+  v = min(v, dpp_u32<0x111, 0xF>(id, v));
+  v = min(v, dpp_u32<0x112, 0xF>(id, v));
+  v = min(v, dpp_u32<0x114, 0xF>(id, v));
+  v = min(v, dpp_u32<0x118, 0xF>(id, v));
+  v = min(v, dpp_u32<0x142, 0xA>(id, v));
+  v = min(v, dpp_u32<0x143, 0xC>(id, v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+
 // Sum across aligned groups of G lanes (G a power of two <= 64).
 template <int G>
 QMOE_D float group_sum(float v) {

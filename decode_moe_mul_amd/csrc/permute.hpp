@@ -1,0 +1,121 @@
+// Stable counting sort of routing assignments by expert id, as one
+// workgroup: shared by moe_permute and the fused decode routing kernel.
+// Wave w of the first W waves owns the contiguous assignment range
+// [w*A/W, (w+1)*A/W):
+//   pass 1: per-wave histogram hist[w][e] in LDS (lanes with the same id are
+//           found with ballots over the id bits; their leader adds the count);
+//   scan:   offsets[e] = sum over e' < e, then per-wave cursors
+//           cursor[w][e] = offsets[e] + sum over w' < w of hist[w'][e];
+//   pass 2: each wave walks its range in order and places assignment a at
+//           cursor[w][e] + (rank of a among equal ids in this 64-chunk).
+// Ascending a within an expert follows from the range order, the chunk order
+// and the lane order, so the result is the unique stable order.  Ids outside
+// [0, E) get no position (inv = -1); perm past the valid count is -1.
+#pragma once
+#include "common.hpp"
+
+namespace qmoe {
+
+QMOE_D uint64_t lanes_below(int lane) { return lane ? (~0ull >> (64 - lane)) : 0ull; }
+
+// Lanes of this wave whose id equals mine (only among `active` lanes).
+QMOE_D uint64_t peers_of(int id, int nbits, uint64_t active) {
+  uint64_t m = active;
+  for (int b = 0; b < nbits; ++b) {
+    const uint64_t on = __ballot((id >> b) & 1);
+    m &= ((id >> b) & 1) ? on : ~on;
+  }
+  return m;
+}
+
+// NT threads; hist holds W*E ints and wsum NT/64 ints of LDS.  ids may live
+// in global memory or LDS.  Called by every thread of the block.
+template <int NT>
+QMOE_D void permute_block(const int32_t* ids, int A, int E, int W, int nbits, int32_t* offsets,
+                          int32_t* perm, int32_t* inv, int* hist, int* wsum) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < W * E; i += NT) hist[i] = 0;
+  __syncthreads();
+  const long long a_begin = (long long)wave * A / W, a_end = (long long)(wave + 1) * A / W;
+  // pass 1: per-wave histogram
+  if (wave < W) {
+    for (long long c = a_begin; c < a_end; c += 64) {
+      const long long a = c + lane;
+      const bool in = a < a_end;
+      const int id = in ? ids[a] : -1;
+      const bool valid = in && id >= 0 && id < E;
+      const uint64_t active = __ballot(valid);
+      const uint64_t peers = peers_of(valid ? id : 0, nbits, active);
+      if (valid && (peers & lanes_below(lane)) == 0)
+        hist[wave * E + id] += __popcll(peers);
+    }
+  }
+  __syncthreads();
+  // scan over experts of the per-expert totals (thread i owns a slice)
+  const int per = (E + NT - 1) / NT;
+  const int e_lo = min(E, threadIdx.x * per), e_hi = min(E, e_lo + per);
+  int local = 0;
+  for (int e = e_lo; e < e_hi; ++e)
+    for (int w = 0; w < W; ++w) local += hist[w * E + e];
+  // inclusive scan of `local` across the block
+  int v = local;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(v, off, 64);
+    if (lane >= off) v += o;
+  }
+  if (lane == 63) wsum[wave] = v;
+  __syncthreads();
+  int wave_base = 0;
+  for (int w = 0; w < wave; ++w) wave_base += wsum[w];
+  int run = wave_base + v - local;  // exclusive prefix for this thread's slice
+  for (int e = e_lo; e < e_hi; ++e) {
+    offsets[e] = run;
+    for (int w = 0; w < W; ++w) {
+      const int c = hist[w * E + e];
+      hist[w * E + e] = run;  // becomes the cursor of wave w for expert e
+      run += c;
+    }
+  }
+  int total = 0;
+  for (int w = 0; w < NT / 64; ++w) total += wsum[w];
+  if (threadIdx.x == 0) offsets[E] = total;
+  __syncthreads();
+  // pass 2: stable scatter within each wave's range
+  if (wave < W) {
+    for (long long c = a_begin; c < a_end; c += 64) {
+      const long long a = c + lane;
+      const bool in = a < a_end;
+      const int id = in ? ids[a] : -1;
+      const bool valid = in && id >= 0 && id < E;
+      const uint64_t active = __ballot(valid);
+      const uint64_t peers = peers_of(valid ? id : 0, nbits, active);
+      if (valid) {
+        const int pos = hist[wave * E + id] + __popcll(peers & lanes_below(lane));
+        perm[pos] = (int32_t)a;
+        inv[a] = pos;
+      } else if (in) {
+        inv[a] = -1;
+      }
+      // all lanes have read their cursor; now the leaders advance it
+      __builtin_amdgcn_wave_barrier();
+      if (valid && (peers & lanes_below(lane)) == 0) hist[wave * E + id] += __popcll(peers);
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+  // positions past the valid ones hold -1
+  for (long long i = (long long)total + threadIdx.x; i < A; i += NT) perm[i] = -1;
+}
+
+// waves of a permute_block over E experts with `lds_ints` ints of LDS for hist
+QMOE_HD int permute_waves(int E, int lds_ints, int max_waves) {
+  int W = lds_ints / E;
+  if (W > max_waves) W = max_waves;
+  return W < 1 ? 1 : W;
+}
+QMOE_HD int id_bits(int E) {
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  return nbits;
+}
+
+}  // namespace qmoe

@@ -97,7 +97,8 @@ class MoELayer:
             A = T * kt
             dev = self.device
             ws = {
-                "route": qmoe.route_workspace(T, c.H, c.E, dev),
+                "route": (qmoe.route_decode_workspace(T, c.H, c.E, dev) if self._fused(T, prefill)
+                          else qmoe.route_workspace(T, c.H, c.E, dev)),
                 "ids": torch.empty((T, kt), dtype=torch.int32, device=dev),
                 "p": torch.empty((T, kt), dtype=torch.float32, device=dev),
                 "offsets": torch.empty(c.E_total + 1, dtype=torch.int32, device=dev),
@@ -111,6 +112,13 @@ class MoELayer:
             self._ws[key] = ws
         return self._ws[key]
 
+    def _fused(self, T, prefill):
+        """Decode rows route and permute in one launch (moe_route_decode)."""
+        c = self.cfg
+        kt = c.k + c.n_shared
+        return (not prefill and T <= 16 and c.E <= 512
+                and ((T * kt + 63) // 64) * 64 + 16 + c.E_total <= 8192)
+
     def forward(self, x, copy=0, prefill=False):
         """y [T, H] for activations x [T, H] (float32 or bfloat16).  The
         intermediate ids, p, offsets, perm, inv, o stay in the workspace dict
@@ -121,12 +129,20 @@ class MoELayer:
         L = qmoe.lib()
         s = qmoe._stream()
         kt = c.k + c.n_shared
-        qmoe._check(L.moe_route(qmoe._p(x), qmoe._dtype_code(x), T, c.H, qmoe._p(self.Wr),
-                                qmoe._p(self.bias), c.E, c.k, c.n_shared, qmoe._p(ws["ids"]),
-                                qmoe._p(ws["p"]), None, qmoe._p(ws["route"]),
-                                ws["route"].numel(), s), "moe_route")
-        qmoe._check(L.moe_permute(qmoe._p(ws["ids"]), T, kt, c.E_total, qmoe._p(ws["offsets"]),
-                                  qmoe._p(ws["perm"]), qmoe._p(ws["inv"]), s), "moe_permute")
+        if self._fused(T, prefill):
+            qmoe._check(L.moe_route_decode(
+                qmoe._p(x), qmoe._dtype_code(x), T, c.H, qmoe._p(self.Wr), qmoe._p(self.bias),
+                c.E, c.k, c.n_shared, qmoe._p(ws["ids"]), qmoe._p(ws["p"]), None,
+                qmoe._p(ws["offsets"]), qmoe._p(ws["perm"]), qmoe._p(ws["inv"]),
+                qmoe._p(ws["route"]), ws["route"].numel(), s), "moe_route_decode")
+        else:
+            qmoe._check(L.moe_route(qmoe._p(x), qmoe._dtype_code(x), T, c.H, qmoe._p(self.Wr),
+                                    qmoe._p(self.bias), c.E, c.k, c.n_shared,
+                                    qmoe._p(ws["ids"]), qmoe._p(ws["p"]), None,
+                                    qmoe._p(ws["route"]), ws["route"].numel(), s), "moe_route")
+            qmoe._check(L.moe_permute(qmoe._p(ws["ids"]), T, kt, c.E_total,
+                                      qmoe._p(ws["offsets"]), qmoe._p(ws["perm"]),
+                                      qmoe._p(ws["inv"]), s), "moe_permute")
         fn = L.qgemm_grouped_prefill if prefill else L.moe_ffn_tiered
         arr = self.tier_arrays[copy]
         qmoe._check(fn(arr, len(arr), c.E_total, c.H, c.F, qmoe._p(x), qmoe._dtype_code(x), T, kt,

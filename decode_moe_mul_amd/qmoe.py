@@ -42,6 +42,9 @@ _SIGNATURES = {
     "moe_route_workspace_size": (_SZ, [_I, _I, _I]),
     "moe_route": (_I, [_VP, _I, _I, _I, _VP, _VP, _I, _I, _I, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "moe_permute": (_I, [_VP, _I, _I, _I, _VP, _VP, _VP, _VP]),
+    "moe_route_decode_workspace_size": (_SZ, [_I, _I, _I]),
+    "moe_route_decode": (_I, [_VP, _I, _I, _I, _VP, _VP, _I, _I, _I, _VP, _VP, _VP, _VP, _VP,
+                              _VP, _VP, _SZ, _VP]),
     "moe_ffn_workspace_size": (_SZ, [_I, _I, _I]),
     "moe_ffn_tiered": (_I, [ctypes.POINTER(Tier), _I, _I, _I, _I, _VP, _I, _I, _I, _VP, _VP,
                             _VP, _VP, _SZ, _VP]),
@@ -204,6 +207,37 @@ def route(x, Wr, bias, k, n_shared=0, logits=False, ws=None):
     _check(lib().moe_route(_p(x), _dtype_code(x), T, H, _p(Wr), _p(bias), E, k, n_shared,
                            _p(ids), _p(p), _p(lg), _p(ws), ws.numel(), _stream()), "moe_route")
     return (ids, p, lg) if logits else (ids, p)
+
+
+def route_decode_workspace(T, H, E, device="cuda"):
+    """Workspace of moe_route_decode: zero-filled, as its counters require."""
+    torch = _torch()
+    n = lib().moe_route_decode_workspace_size(T, H, E)
+    return torch.zeros(max(int(n), 1), dtype=torch.uint8, device=device)
+
+
+def route_decode(x, Wr, bias, k, n_shared=0, logits=False, ws=None):
+    """moe_route + moe_permute in one launch (T <= 16):
+    ids, p, offsets, perm, inv_perm (and logits [T, E])."""
+    torch = _torch()
+    _cuda_contig(x, Wr, bias)
+    T, H = x.shape
+    E = Wr.shape[0]
+    kt = k + n_shared
+    dev = x.device
+    ids = torch.empty((T, kt), dtype=torch.int32, device=dev)
+    p = torch.empty((T, kt), dtype=torch.float32, device=dev)
+    lg = torch.empty((T, E), dtype=torch.float32, device=dev) if logits else None
+    offsets = torch.empty(E + n_shared + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(max(T * kt, 1), dtype=torch.int32, device=dev)
+    inv = torch.empty(max(T * kt, 1), dtype=torch.int32, device=dev)
+    if ws is None:
+        ws = route_decode_workspace(T, H, E, dev)
+    _check(lib().moe_route_decode(_p(x), _dtype_code(x), T, H, _p(Wr), _p(bias), E, k, n_shared,
+                                  _p(ids), _p(p), _p(lg), _p(offsets), _p(perm), _p(inv),
+                                  _p(ws), ws.numel(), _stream()), "moe_route_decode")
+    out = (ids, p, offsets, perm, inv)
+    return out + (lg,) if logits else out
 
 
 def permute(ids, E, out=None):

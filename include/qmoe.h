@@ -166,6 +166,26 @@ int moe_route(const void *x, int x_dtype, int T, int H, const float *Wr,
               const float *bias, int E, int k, int n_shared, int32_t *ids,
               float *p, float *logits, void *ws, size_t ws_bytes, void *stream);
 
+/* moe_route_decode: moe_route followed by moe_permute(ids, T, k + n_shared,
+ * E + n_shared, offsets, perm, inv_perm) in a single launch, for decode rows.
+ * Outputs (ids, p, logits when not NULL, offsets, perm, inv_perm) are
+ * identical to those two calls, bit for bit.  Inside the launch the block that
+ * finishes last (a device-scope counter in the workspace decides) sums the
+ * split-K router partials, takes the top-k of every row and sorts the
+ * assignments, so the routing of a decode step is one launch instead of three.
+ * Limits: as moe_route, plus T <= 16, E <= 512 and
+ * round_up(T*(k+n_shared), 64) + E + n_shared <= 8176 (UNSUPPORTED beyond).
+ * T == 0 writes zero offsets and nothing else.
+ * Workspace: moe_route_decode_workspace_size(T, H, E) bytes, 256-byte
+ * aligned, whose first 256 bytes must be zero before the first call that uses
+ * it; every call leaves them zero again.  Calls sharing one workspace must not
+ * run concurrently.  */
+size_t moe_route_decode_workspace_size(int T, int H, int E);
+int moe_route_decode(const void *x, int x_dtype, int T, int H, const float *Wr,
+                     const float *bias, int E, int k, int n_shared, int32_t *ids,
+                     float *p, float *logits, int32_t *offsets, int32_t *perm,
+                     int32_t *inv_perm, void *ws, size_t ws_bytes, void *stream);
+
 /* moe_permute: stable counting sort of the flat assignments a = t*k + i by
  * expert id ([P2] "优化策略三" groups a layer's routed tokens by expert; bug
  * item 1 shows grouping must survive duplicate ids).

@@ -77,6 +77,17 @@ def test_host_validation_rejects_before_launch(L):
     need = L.moe_route_workspace_size(4, 64, 16)
     assert need > 0
     assert L.moe_route(fake, 0, 4, 64, fake, None, 16, 2, 0, fake, fake, None, fake, need - 1, None) == -3
+    # fused decode routing: too many rows, workspace too small
+    need = L.moe_route_decode_workspace_size(4, 64, 16)
+    assert need >= L.moe_route_workspace_size(4, 64, 16)
+    assert L.moe_route_decode(fake, 0, 17, 64, fake, None, 16, 2, 0, fake, fake, None, fake,
+                              fake, fake, fake, 1 << 30, None) == -2
+    assert L.moe_route_decode(fake, 0, 4, 64, fake, None, 16, 2, 0, fake, fake, None, fake,
+                              fake, fake, fake, need - 1, None) == -3
+    assert L.moe_route_decode(fake, 0, 16, 64, fake, None, 512, 64, 8000, fake, fake, None,
+                              fake, fake, fake, fake, 1 << 30, None) == -2
+    assert L.moe_route_decode(fake, 0, 1, 64, fake, None, 513, 8, 0, fake, fake, None,
+                              fake, fake, fake, fake, 1 << 30, None) == -2
     # permute: E too large
     assert L.moe_permute(fake, 4, 2, 9000, fake, fake, fake, None) == -2
     # combine: H not a multiple of 4

@@ -149,3 +149,69 @@ def test_permute_is_deterministic_and_stable_under_repeat():
     a = [to_np(t) for t in qmoe.permute(ids, 512)]
     b = [to_np(t) for t in qmoe.permute(ids, 512)]
     assert all((x == y).all() for x, y in zip(a, b))
+
+
+# ------------------------------------------------- fused decode routing ---
+
+def _route_decode_vs_two_calls(x, Wr, b, k, n_shared=0, ws=None):
+    """moe_route_decode must reproduce moe_route + moe_permute bit for bit
+    (same fp32 sums in the same order, same top-k and the same sort)."""
+    E = Wr.shape[0]
+    ids, p, lg = qmoe.route(x, Wr, b, k, n_shared=n_shared, logits=True)
+    off, perm, inv = qmoe.permute(ids, E + n_shared)
+    got = qmoe.route_decode(x, Wr, b, k, n_shared=n_shared, logits=True, ws=ws)
+    want = (ids, p, off, perm, inv, lg)
+    for name, g, w in zip(("ids", "p", "offsets", "perm", "inv", "logits"), got, want):
+        g, w = to_np(g), to_np(w)
+        assert g.shape == w.shape, name
+        assert np.array_equal(g, w, equal_nan=True), name
+    # and the permutation is the oracle's sort of those ids
+    off_r, perm_r, inv_r = moe.permute(to_np(ids), E + n_shared)
+    assert (to_np(got[2]) == off_r).all() and (to_np(got[3]) == perm_r).all()
+    assert (to_np(got[4]) == inv_r).all()
+    return got
+
+
+@pytest.mark.parametrize("T,H,E,k,bias,n_shared,dt", [
+    (1, 2048, 512, 10, True, 0, "f32"), (6, 2048, 512, 10, True, 0, "f32"),
+    (16, 7168, 256, 8, False, 1, "bf16"), (4, 512, 16, 2, False, 0, "f32"),
+    (3, 256, 40, 5, False, 2, "f32"), (16, 4096, 512, 8, True, 0, "bf16"), (2, 1024, 500, 6, True, 3, "f32"),
+    (1, 7168, 1, 1, False, 0, "f32"), (9, 3072, 129, 64, False, 0, "f32")])
+def test_route_decode_matches_route_then_permute(T, H, E, k, bias, n_shared, dt):
+    x = synth.normal((T, H), 1.0, 11, synth.ACT, T)
+    Wr = synth.normal((E, H), 0.02, 11, synth.ROUTER)
+    b = to_gpu(synth.rank_prior(E, 0.5)) if bias else None
+    xg = to_gpu(x) if dt == "f32" else to_gpu(x).to(torch.bfloat16)
+    _route_decode_vs_two_calls(xg, to_gpu(Wr), b, k, n_shared)
+
+
+def test_route_decode_ties_and_nan():
+    T, H, E, k = 8, 256, 64, 6
+    x = synth.normal((T, H), 1.0, 3, synth.ACT)
+    Wr = synth.normal((E, H), 0.02, 3, synth.ROUTER)
+    Wr[7] = np.float32(0.05) * x.mean(0)
+    Wr[40] = Wr[7]
+    Wr[63] = Wr[7]
+    x[5, 3] = np.nan
+    got = _route_decode_vs_two_calls(to_gpu(x), to_gpu(Wr), None, k)
+    assert list(to_np(got[0])[5]) == [0, 1, 2, 3, 4, 5]
+
+
+def test_route_decode_reuses_its_workspace():
+    """The workspace counters return to zero: back-to-back calls on one
+    workspace, with different inputs and fewer rows, stay exact."""
+    H, E, k = 2048, 512, 10
+    ws = qmoe.route_decode_workspace(16, H, E)
+    Wr = to_gpu(synth.normal((E, H), 0.02, 12, synth.ROUTER))
+    for i, T in enumerate((16, 16, 5, 1, 16)):
+        x = to_gpu(synth.normal((T, H), 1.0, 20 + i, synth.ACT, T))
+        _route_decode_vs_two_calls(x, Wr, None, k, ws=ws)
+    assert (to_np(ws[:256]) == 0).all()
+
+
+def test_route_decode_zero_rows_zero_offsets():
+    Wr = to_gpu(synth.normal((32, 256), 0.02, 1, synth.ROUTER))
+    x = torch.zeros((0, 256), dtype=torch.float32, device="cuda")
+    ids, p, off, perm, inv = qmoe.route_decode(x, Wr, None, 4, n_shared=1)
+    torch.cuda.synchronize()
+    assert off.shape == (34,) and (to_np(off) == 0).all()
