@@ -84,6 +84,14 @@ QMOE_D float fdot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, a), __builtin_bit_cast(h2_t, b), c, false);
 }
 // 2^(e-127) for an E8M0 byte; 255 is NaN; e = 0 is the fp32 subnormal 2^-127
+// Weight bytes are read once per call: the nontemporal hint streams them
+// past the caches instead of displacing lines that are reused.
+QMOE_D uint4 load_stream(const void* p) {
+  typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+  const v4u t = __builtin_nontemporal_load((const v4u*)p);
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+
 QMOE_D float e8m0_to_f32(uint32_t e) {
   uint32_t bits = e == 255u ? 0x7FC00000u : (e == 0u ? 0x00400000u : (e << 23));
   return __builtin_bit_cast(float, bits);

@@ -71,20 +71,20 @@ struct Unit {
     const size_t nb32 = (size_t)(K >> 5);
     if constexpr (FMT == QMOE_Q8_0) {
       const uint4* p = (const uint4*)(M.p0 + (size_t)row * K + 32 * (size_t)u);
-      q = p[0];
-      q2 = p[1];
+      q = load_stream(p);
+      q2 = load_stream(p + 1);
       s0 = ((const uint16_t*)M.p1)[row * nb32 + u];
     } else if constexpr (FMT == QMOE_Q4_0) {
-      q = *(const uint4*)(M.p0 + (size_t)row * (K >> 1) + 16 * (size_t)u);
+      q = load_stream(M.p0 + (size_t)row * (K >> 1) + 16 * (size_t)u);
       s0 = ((const uint16_t*)M.p1)[row * nb32 + u];
     } else if constexpr (FMT == QMOE_MXFP4) {
-      q = *(const uint4*)(M.p0 + (size_t)row * (K >> 1) + 16 * (size_t)u);
+      q = load_stream(M.p0 + (size_t)row * (K >> 1) + 16 * (size_t)u);
       s0 = M.p1[row * nb32 + u];
     } else if constexpr (FMT == QMOE_Q4_K) {
-      q = *(const uint4*)(M.p0 + (size_t)row * (K >> 1) + 16 * (size_t)u);
+      q = load_stream(M.p0 + (size_t)row * (K >> 1) + 16 * (size_t)u);
       meta = ((const uint4*)M.p1)[(size_t)row * (K >> 8) + (u >> 3)];
     } else {
-      q = *(const uint4*)(M.p0 + (size_t)row * (K >> 1) + 16 * (size_t)u);
+      q = load_stream(M.p0 + (size_t)row * (K >> 1) + 16 * (size_t)u);
       qh = *(const uint2*)(M.p1 + (size_t)row * (K >> 2) + 8 * (size_t)u);
       const size_t sb = (size_t)row * (K >> 8) + (u >> 3);
       // the aligned word holding the unit's two sub-block scales (bytes
