@@ -198,6 +198,91 @@ def summarize_pmc(fetch_dir, write_dir):
     print(json.dumps(out, indent=1))
 
 
+def _events_ms(torch, fn, n):
+    stream = torch.cuda.current_stream()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(n):
+        fn(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / n
+
+
+def dense_gemv(torch, steps):
+    """One dense decoder layer's quantized matrices at one fp32 row (Q, K, V,
+    O, gate, up in Q4_K; down in Q6_K; Llama-3-8B shapes): qgemv per matrix,
+    8 weight copies rotated so the last-level cache cannot serve them."""
+    from decode_moe_mul_amd import configs, layers, synth
+    from decode_moe_mul_amd import qmoe
+    layer = layers.DenseLayer(configs.LLAMA8B_GEMV, copies=8)
+    x = torch.from_numpy(synth.normal((1, 4096), 1.0, 3, synth.ACT, 0)).cuda()
+    xd = {"down": torch.from_numpy(synth.normal((1, 14336), 1.0, 3, synth.ACT, 1)).cuda()}
+    xs = {n: (xd["down"] if n == "down" else x) for (n, _, _, _) in configs.LLAMA8B_GEMV.mats}
+    for i in range(16):
+        layer.forward(xs, i % 8)
+    ms = _events_ms(torch, lambda i: layer.forward(xs, i % 8), steps)
+    qmoe.profile_reset()
+    qmoe.profile_enable(True)
+    _events_ms(torch, lambda i: layer.forward(xs, i % 8), steps)
+    qmoe.profile_enable(False)
+    n, kms = qmoe.profile_read("qgemv")
+    nbytes = layer.weight_bytes()
+    kernel_ms = kms / steps
+    del layer
+    torch.cuda.empty_cache()
+    log(f"dense layer gemv: {ms * 1e3:.1f} us per token ({kernel_ms * 1e3:.1f} us in kernels)")
+    return {"workload": "llama3_8b_layer_gemv Q4_K x6 + Q6_K down, 1 fp32 row",
+            "weight_bytes": int(nbytes), "us_per_token": round(ms * 1e3, 2),
+            "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "kernel_us": round(kernel_ms * 1e3, 2),
+            "kernel_gbs": round(nbytes / (kernel_ms * 1e-3) / 1e9, 1),
+            "kernel_hbm_frac": round(nbytes / (kernel_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
+def prefill_chunk(torch, calls=10):
+    """The tiered 512-expert layer on a 2048-row prefill chunk: router GEMM,
+    top-k, permutation, grouped gate/up and down on the matrix cores, combine.
+    Reports the HBM rate on the weight bytes of the experts touched and the
+    matrix-core utilisation (useful flops of the expert GEMMs / time / dense
+    bf16 peak)."""
+    from decode_moe_mul_amd import configs, layers, synth
+    from decode_moe_mul_amd import qmoe
+    cfg = configs.PREFILL
+    layer = layers.MoELayer(cfg, copies=2)
+    T = 2048
+    x = torch.from_numpy(synth.normal((T, cfg.H), 1.0, 4, synth.ACT, 0)).cuda()
+    _, ws = layer.forward(x, 0, prefill=True)
+    ids = ws["ids"].cpu().numpy()
+    nbytes = layer.weight_bytes(ids)
+    A = T * (cfg.k + cfg.n_shared)
+    flops = 2.0 * A * 3 * cfg.F * cfg.H
+    for i in range(3):
+        layer.forward(x, i % 2, prefill=True)
+    ms = _events_ms(torch, lambda i: layer.forward(x, i % 2, prefill=True), calls)
+    qmoe.profile_reset()
+    qmoe.profile_enable(True)
+    _events_ms(torch, lambda i: layer.forward(x, i % 2, prefill=True), calls)
+    qmoe.profile_enable(False)
+    kern = {k: qmoe.profile_read(k)[1] / calls for k in
+            ("router_gemm", "topk", "permute", "prefill_schedule", "prefill_gate_up",
+             "prefill_down", "combine")}
+    gemm_ms = kern["prefill_gate_up"] + kern["prefill_down"]
+    del layer
+    torch.cuda.empty_cache()
+    log(f"prefill 2048 rows: {ms:.3f} ms per call (expert GEMMs {gemm_ms:.3f} ms)")
+    return {"workload": "prefill2048_tiered_e512_top10 H=2048 F=640, fp32 rows",
+            "ms_per_call": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
+            "weight_bytes": int(nbytes), "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "expert_gemm_ms": round(gemm_ms, 4),
+            "useful_gflop": round(flops / 1e9, 2),
+            "mfma_util": round(flops / (gemm_ms * 1e-3) / 2.5e15, 4),
+            "mfma_util_whole_call": round(flops / (ms * 1e-3) / 2.5e15, 4),
+            "kernel_ms": {k: round(v, 4) for k, v in kern.items()}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -288,6 +373,9 @@ def main():
                  ("route_decode", "router_gemv", "topk", "permute", "ffn_gate_up", "ffn_down",
                   "combine")}
 
+    dense = dense_gemv(torch, a.steps)
+    prefill = prefill_chunk(torch)
+
     t = stored_traffic()
     traffic = None if t is None else int(t["traffic_bytes_per_launch"])
     total_bytes = float(np.sum(per_step_bytes))
@@ -325,6 +413,8 @@ def main():
                      "avg_launch_us": round(gu_ms * 1e3 / max(n_gu, 1), 3),
                      "algorithmic_bytes_per_launch": int(np.sum(gate_up_bytes) / max(n_gu, 1))},
     }
+    out["dense_gemv"] = dense
+    out["prefill"] = prefill
     if not a.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         out["cpu_baseline"] = cpu_baseline()
