@@ -8,7 +8,8 @@
 //  router_gemv_kernel  rows <= 16: 16 waves per block, each streaming one
 //                      expert row of Wr over a K-slice against all rows
 //                      staged in LDS; split-K partials go to the workspace.
-//  router_gemm_kernel  longer chunks: 64x64 output tiles, LDS-staged K steps.
+//  router_gemm_kernel  longer chunks: 64x64 output tiles on the matrix cores
+//                      (fp32 operands and sums).
 //  topk_kernel         one wave per row: sums the split-K partials in fixed
 //                      order, adds the bias, selects k by repeated wave
 //                      arg-max, softmax over the kept logits.
@@ -170,42 +171,83 @@ __global__ __launch_bounds__(kGemvBlock) void router_gemv_kernel(RouteParams P) 
   router_partials<false>(P, xsl);
 }
 
-// 64 x 64 tile of logits (rows x experts), 256 threads x (4 x 4) outputs.
-constexpr int kGT = 64, kGE = 64, kGK = 32;
-__global__ __launch_bounds__(kRouteBlock) void router_gemm_kernel(RouteParams P) {
-  __shared__ float xs[kGK][kGT + 4];
-  __shared__ float wsm[kGK][kGE + 4];
-  const int t0 = blockIdx.y * kGT, e0 = blockIdx.x * kGE;
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;  // 16 x 16 threads
-  float acc[4][4] = {};
-  for (int k0 = 0; k0 < P.H; k0 += kGK) {
-    for (int i = threadIdx.x; i < kGT * kGK; i += kRouteBlock) {
-      const int r = i / kGK, c = i - r * kGK;
-      const int t = t0 + r, kk = k0 + c;
-      xs[c][r] = (t < P.T && kk < P.H) ? load_act(P.x, P.x_dtype, (size_t)t * P.H + kk) : 0.f;
-      const int e = e0 + r;
-      wsm[c][r] = (e < P.E && kk < P.H) ? P.Wr[(size_t)e * P.H + kk] : 0.f;
-    }
-    __syncthreads();
-#pragma unroll 8
-    for (int c = 0; c < kGK; ++c) {
-      float a[4], b[4];
+// 64 x 64 tile of logits (rows x experts) on the matrix cores in fp32
+// (v_mfma_f32_16x16x4_f32, fp32 products and sums).  Wave w computes rows
+// 32 (w >> 1) .. and experts 32 (w & 1) .. of the tile as 2 x 2 blocks of
+// 16 x 16.  Per 16-wide chunk of H each lane loads 4 consecutive values of
+// its row of x and of its expert's row of Wr; op s of the chunk takes value s
+// of every lane group, so both operands walk the chunk's 16 indices in the
+// same interleaved order.  Four chunks of loads are in flight.
+constexpr int kGT = 64, kGE = 64, kGDepth = 4;
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <int DT>
+QMOE_D void rg_load(const RouteParams& P, const int (&trow)[2], const int (&erow)[2], int k,
+                    float4 (&a)[2], float4 (&b)[2]) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) { a[i] = xs[c][ty + 16 * i]; b[i] = wsm[c][tx + 16 * i]; }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] += a[i] * b[j];
-    }
-    __syncthreads();
+  for (int i = 0; i < 2; ++i) {
+    a[i] = load_act4<DT>(P.x, (size_t)trow[i] * P.H + k);
+    b[i] = *(const float4*)(P.Wr + (size_t)erow[i] * P.H + k);
   }
+}
+
+template <int DT>
+__global__ __launch_bounds__(kRouteBlock) void router_gemm_kernel(RouteParams P) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, kg = lane >> 4;
+  const int tb = blockIdx.y * kGT + 32 * (wave >> 1), eb = blockIdx.x * kGE + 32 * (wave & 1);
+  // operand rows, clamped: rows past the end re-read the last one (dropped)
+  int trow[2], erow[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i) {
+    trow[i] = min(tb + 16 * i + r, P.T - 1);
+    erow[i] = min(eb + 16 * i + r, P.E - 1);
+  }
+  const int nch = (P.H + 15) / 16;
+  // this lane's 4 values of chunk c start at k; past H (when H % 16 != 0)
+  // the load re-reads the last 4 and the values are zeroed
+  auto k_of = [&](int c) { return min(16 * c + 4 * kg, P.H - 4); };
+  f32x4_t acc[2][2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int t = t0 + ty + 16 * i, e = e0 + tx + 16 * j;
-      if (t < P.T && e < P.E) P.part[(size_t)t * P.E + e] = acc[i][j];
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float4 ra[kGDepth][2], rb[kGDepth][2];
+#pragma unroll
+  for (int u = 0; u < kGDepth; ++u) rg_load<DT>(P, trow, erow, k_of(min(u, nch - 1)), ra[u], rb[u]);
+  for (int c0 = 0; c0 < nch; c0 += kGDepth) {
+#pragma unroll
+    for (int u = 0; u < kGDepth; ++u) {
+      const int c = c0 + u;
+      const bool valid = c < nch && 16 * c + 4 * kg < P.H;
+      float4 a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        a[i] = valid ? ra[u][i] : make_float4(0.f, 0.f, 0.f, 0.f);
+        b[i] = rb[u][i];
+      }
+      rg_load<DT>(P, trow, erow, k_of(min(c + kGDepth, nch - 1)), ra[u], rb[u]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i].x, b[j].x, acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i].y, b[j].y, acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i].z, b[j].z, acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i].w, b[j].w, acc[i][j], 0, 0, 0);
+        }
     }
+  }
+  // lane holds rows 4 kg + q of each 16 x 16 block, column r
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int t = tb + 16 * i + 4 * kg + q, e = eb + 16 * j + r;
+        if (t < P.T && e < P.E) P.part[(size_t)t * P.E + e] = acc[i][j][q];
+      }
 }
 
 // Order-preserving unsigned image of a logit (NaN ranks as -inf); every
@@ -457,7 +499,9 @@ int moe_route(const void* x, int x_dtype, int T, int H, const float* Wr, const f
                      (size_t)T * P.ks_len * sizeof(float), s, P);
   } else {
     const dim3 grid((E + kGE - 1) / kGE, (T + kGT - 1) / kGT);
-    st = QMOE_LAUNCH("router_gemm", router_gemm_kernel, grid, kRouteBlock, 0, s, P);
+    st = x_dtype == QMOE_F32
+             ? QMOE_LAUNCH("router_gemm", router_gemm_kernel<QMOE_F32>, grid, kRouteBlock, 0, s, P)
+             : QMOE_LAUNCH("router_gemm", router_gemm_kernel<QMOE_BF16>, grid, kRouteBlock, 0, s, P);
   }
   if (st) return st;
   const dim3 tgrid((T + 3) / 4);
