@@ -213,33 +213,39 @@ def _events_ms(torch, fn, n):
 
 def dense_gemv(torch, steps):
     """One dense decoder layer's quantized matrices at one fp32 row (Q, K, V,
-    O, gate, up in Q4_K; down in Q6_K; Llama-3-8B shapes): qgemv per matrix,
-    8 weight copies rotated so the last-level cache cannot serve them."""
+    O, gate, up in Q4_K; down in Q6_K; Llama-3-8B shapes), 8 weight copies
+    rotated so the last-level cache cannot serve them: one qgemv launch per
+    matrix, and all seven in one qgemv_batch launch."""
     from decode_moe_mul_amd import configs, layers, synth
     from decode_moe_mul_amd import qmoe
     layer = layers.DenseLayer(configs.LLAMA8B_GEMV, copies=8)
     x = torch.from_numpy(synth.normal((1, 4096), 1.0, 3, synth.ACT, 0)).cuda()
-    xd = {"down": torch.from_numpy(synth.normal((1, 14336), 1.0, 3, synth.ACT, 1)).cuda()}
-    xs = {n: (xd["down"] if n == "down" else x) for (n, _, _, _) in configs.LLAMA8B_GEMV.mats}
-    for i in range(16):
-        layer.forward(xs, i % 8)
-    ms = _events_ms(torch, lambda i: layer.forward(xs, i % 8), steps)
-    qmoe.profile_reset()
-    qmoe.profile_enable(True)
-    _events_ms(torch, lambda i: layer.forward(xs, i % 8), steps)
-    qmoe.profile_enable(False)
-    n, kms = qmoe.profile_read("qgemv")
+    xd = torch.from_numpy(synth.normal((1, 14336), 1.0, 3, synth.ACT, 1)).cuda()
+    xs = {n: (xd if n == "down" else x) for (n, _, _, _) in configs.LLAMA8B_GEMV.mats}
     nbytes = layer.weight_bytes()
-    kernel_ms = kms / steps
+    res = {"workload": "llama3_8b_layer_gemv Q4_K x6 + Q6_K down, 1 fp32 row",
+           "weight_bytes": int(nbytes)}
+    for mode, batched in (("per_matrix", False), ("batched", True)):
+        fwd = lambda i: layer.forward(xs, i % 8, batched=batched)
+        for i in range(16):
+            fwd(i)
+        ms = _events_ms(torch, fwd, steps)
+        qmoe.profile_reset()
+        qmoe.profile_enable(True)
+        _events_ms(torch, fwd, steps)
+        qmoe.profile_enable(False)
+        n, kms = qmoe.profile_read("qgemv")
+        kernel_ms = kms / steps
+        log(f"dense layer gemv ({mode}): {ms * 1e3:.1f} us per token "
+            f"({kernel_ms * 1e3:.1f} us in kernels)")
+        res[mode] = {"us_per_token": round(ms * 1e3, 2),
+                     "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                     "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "kernel_us": round(kernel_ms * 1e3, 2),
+                     "kernel_gbs": round(nbytes / (kernel_ms * 1e-3) / 1e9, 1)}
     del layer
     torch.cuda.empty_cache()
-    log(f"dense layer gemv: {ms * 1e3:.1f} us per token ({kernel_ms * 1e3:.1f} us in kernels)")
-    return {"workload": "llama3_8b_layer_gemv Q4_K x6 + Q6_K down, 1 fp32 row",
-            "weight_bytes": int(nbytes), "us_per_token": round(ms * 1e3, 2),
-            "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
-            "kernel_us": round(kernel_ms * 1e3, 2),
-            "kernel_gbs": round(nbytes / (kernel_ms * 1e-3) / 1e9, 1),
-            "kernel_hbm_frac": round(nbytes / (kernel_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    return res
 
 
 def prefill_chunk(torch, calls=10):

@@ -26,6 +26,8 @@
 //    dequantized in registers, v_mfma_f32_16x16x32_f16.
 //  * Gate and up rows of the same output are handled by the same lanes, so
 //    SiLU(g) * u is applied in registers before anything is stored.
+#include <algorithm>
+
 #include "common.hpp"
 #include "dequant.hpp"
 
@@ -413,15 +415,16 @@ QMOE_D void valu_pass(const Mat (&mats)[NMAT], int K, int rb, int re, int G, int
   }
 }
 
-// Stage up to RC rows at a time and stream the tile against them.
+// Stage up to `chunk` (<= RC) rows at a time and stream the tile against
+// them.
 template <int FMT, int NMAT, int RC, class SrcOf, class SinkOf>
 QMOE_D void valu_rows(const Mat (&mats)[NMAT], int K, int rb, int re, int G, int rows_total,
-                      int dtype, uint8_t* lds, SrcOf src_of, SinkOf sink_of) {
+                      int dtype, uint8_t* lds, SrcOf src_of, SinkOf sink_of, int chunk = RC) {
   const int U = K >> 5;
   uint8_t* xs = lds;
-  float2* sb = (float2*)(lds + (size_t)RC * tok_stride(U));
-  for (int c0 = 0; c0 < rows_total; c0 += RC) {
-    const int rc = min(RC, rows_total - c0);
+  float2* sb = (float2*)(lds + (size_t)chunk * tok_stride(U));
+  for (int c0 = 0; c0 < rows_total; c0 += chunk) {
+    const int rc = min(chunk, rows_total - c0);
     __syncthreads();
     stage_rows<FMT>(xs, sb, rc, U, [&](int r) { return src_of(c0 + r); }, dtype);
     __syncthreads();
@@ -709,6 +712,65 @@ __global__ __launch_bounds__(kBlock) void qgemv_kernel(GemvParams P) {
     valu_rows<FMT, 1, RC>(mats, K, rb, re, P.G, P.R, dtype, smem, src, sink);
 }
 
+// ------------------------------------------------ batched dense GEMV ----
+// Several independent matrices in one launch: block b serves matrix i with
+// block_off[i] <= b < block_off[i + 1] and row tile b - block_off[i].  Each
+// matrix is processed exactly as qgemv would (same lanes per row, same
+// register blocking), so its output equals qgemv's bit for bit.
+struct GemvBatchParams {
+  qmoe_gemv_desc d[QMOE_MAX_BATCH];
+  int G[QMOE_MAX_BATCH], tile_rows[QMOE_MAX_BATCH];
+  int rc[QMOE_MAX_BATCH];  // rows per dot-product chunk; 0: matrix cores
+  int block_off[QMOE_MAX_BATCH + 1];
+  int n;
+};
+
+template <int RC, bool MFMA>
+__global__ __launch_bounds__(kBlock) void qgemv_batch_kernel(GemvBatchParams P) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  // matrix of this block, its fields taken with constant indices only (a
+  // runtime index into the by-value argument would spill it to scratch)
+  const int b = blockIdx.x;
+  int fmt = 0, N = 0, K = 0, dtype = 0, R = 0, G = 1, tr = 1, boff = 0, rc = 1;
+  const void* W = nullptr;
+  const void* x = nullptr;
+  float* y = nullptr;
+#pragma unroll
+  for (int i = 0; i < QMOE_MAX_BATCH; ++i) {
+    if (i < P.n && b >= P.block_off[i] && b < P.block_off[i + 1]) {
+      fmt = P.d[i].fmt; N = P.d[i].N; K = P.d[i].K; dtype = P.d[i].x_dtype; R = P.d[i].R;
+      W = P.d[i].W; x = P.d[i].x; y = P.d[i].y;
+      G = P.G[i]; tr = P.tile_rows[i]; boff = P.block_off[i]; rc = P.rc[i];
+    }
+  }
+  if (!W) return;
+  const int rb = (b - boff) * tr, re = min(N, rb + tr);
+  if (rb >= re) return;
+  const char* xb = (const char*)x;
+  const size_t xrow_bytes = (size_t)K * (dtype == QMOE_F32 ? 4 : 2);
+  auto src = [=](int r) { return (const void*)(xb + (size_t)r * xrow_bytes); };
+  auto sink = [=](int n, int r, const float* a) { y[(size_t)r * N + n] = a[0]; };
+#define QMOE_BATCH_CASE(FM)                                                      \
+  case FM: {                                                                     \
+    const Mat mats[1] = {mat_of(W, FM, N, K)};                                   \
+    if (MFMA && rc == 0 && dtype == QMOE_F32)                                    \
+      mfma_cols<FM, 1, QMOE_F32>(mats, K, rb, re, R, smem, src, sink);           \
+    else if (MFMA && rc == 0)                                                    \
+      mfma_cols<FM, 1, QMOE_BF16>(mats, K, rb, re, R, smem, src, sink);          \
+    else                                                                         \
+      valu_rows<FM, 1, RC>(mats, K, rb, re, G, R, dtype, smem, src, sink, rc);   \
+  } break;
+  switch (fmt) {
+    QMOE_BATCH_CASE(QMOE_Q8_0)
+    QMOE_BATCH_CASE(QMOE_Q4_0)
+    QMOE_BATCH_CASE(QMOE_MXFP4)
+    QMOE_BATCH_CASE(QMOE_Q4_K)
+    QMOE_BATCH_CASE(QMOE_Q6_K)
+    default: break;
+  }
+#undef QMOE_BATCH_CASE
+}
+
 // ------------------------------------------------------- routed FFN -----
 struct FfnParams {
   qmoe_tier tiers[QMOE_MAX_TIERS];
@@ -915,6 +977,26 @@ static int pick_tile_rows(int N, int G, int work_items) {
   return (rows + group - 1) / group * group;
 }
 
+// Rows per block for a dense matrix of mat_bytes in a launch that streams
+// total_bytes: about eight blocks per compute unit overall, but no fewer than
+// kMinBlockBytes of weights per block, since every block stages its own copy
+// of the activation rows; each matrix gets blocks in proportion to its bytes.
+// A multiple of a wave pass and of the 16-row matrix-core blocks.
+constexpr size_t kMinBlockBytes = 64 << 10;
+static int pick_tile_rows_bytes(int N, int G, size_t mat_bytes, size_t total_bytes) {
+  int group = kWaves * (64 / G);
+  if (group < 16) group = 16;
+  int cus = cu_count();
+  if (cus <= 0) cus = 256;
+  const long long by_bytes = (long long)(total_bytes / kMinBlockBytes);
+  const long long blocks = std::min<long long>(8LL * cus, std::max<long long>(cus, by_bytes));
+  long long tiles = total_bytes ? (long long)((double)blocks * mat_bytes / total_bytes) : 1;
+  const long long max_tiles = (N + group - 1) / group;
+  tiles = std::max<long long>(1, std::min(tiles, max_tiles));
+  const int rows = (int)((N + tiles - 1) / tiles);
+  return (rows + group - 1) / group * group;
+}
+
 template <int FMT>
 static int qgemv_dispatch(const GemvParams& P, int RC, dim3 grid, size_t lds, hipStream_t s) {
   if (P.R > RC) return QMOE_LAUNCH("qgemv", (qgemv_kernel<FMT, 4, true>), grid, kBlock, lds, s, P);
@@ -937,7 +1019,8 @@ static int qgemv_launch(int FMT, const void* W, int N, int K, const void* x, int
   // more rows than RC) take the matrix-core path, which stages nothing
   const int RC = pick_rc(R, K);
   GemvParams P{W, N, K, x, x_dtype, R, y, lanes_per_row(K), 0};
-  P.tile_rows = pick_tile_rows(N, P.G, 1);
+  const size_t wbytes = layout_of(FMT, N, K).total;
+  P.tile_rows = pick_tile_rows_bytes(N, P.G, wbytes, wbytes);
   if (R > RC) {  // matrix-core tiles: whole 64-column passes
     const int pass = 16 * mfma_cols_per_pass(1);
     P.tile_rows = (P.tile_rows + pass - 1) / pass * pass;
@@ -952,6 +1035,72 @@ static int qgemv_launch(int FMT, const void* W, int N, int K, const void* x, int
     case QMOE_Q4_K: return qgemv_dispatch<QMOE_Q4_K>(P, RC, grid, lds, s);
     default: return qgemv_dispatch<QMOE_Q6_K>(P, RC, grid, lds, s);
   }
+}
+
+// Batched GEMV: each matrix is checked as qgemv checks it and takes the path
+// qgemv would take for it (dot products in chunks of pick_rc(R, K) rows, or
+// the matrix cores beyond), with qgemv's lanes per row, so its arithmetic
+// matches qgemv's exactly.  The kernel's register blocking is the largest
+// chunk of the batch, its LDS the largest staging.
+static int qgemv_batch_launch(const qmoe_gemv_desc* d, int n, void* stream) {
+  if (n < 0 || n > QMOE_MAX_BATCH)
+    return fail(QMOE_ERR_INVALID_ARG, "qgemv_batch: n=%d outside [0, %d]", n, QMOE_MAX_BATCH);
+  if (n == 0) return QMOE_OK;
+  if (!d) return fail(QMOE_ERR_INVALID_ARG, "qgemv_batch: null descriptors");
+  GemvBatchParams P{};
+  P.n = n;
+  bool any_mfma = false;
+  long long blocks = 0;
+  for (int i = 0; i < n; ++i) {
+    const qmoe_gemv_desc& q = d[i];
+    if (!block_of(q.fmt)) return fail(QMOE_ERR_UNSUPPORTED, "qgemv_batch: matrix %d unknown format", i);
+    const bool work = q.N > 0 && q.R > 0;  // empty products touch no memory
+    if (work && (!q.W || !q.x || !q.y))
+      return fail(QMOE_ERR_INVALID_ARG, "qgemv_batch: matrix %d null pointer", i);
+    if (q.N < 0 || q.K <= 0 || q.R < 0 || q.R > 16 || q.K % block_of(q.fmt) || q.K > 65536)
+      return fail(QMOE_ERR_INVALID_ARG, "qgemv_batch: matrix %d bad sizes N=%d K=%d R=%d", i, q.N,
+                  q.K, q.R);
+    if (q.x_dtype != QMOE_F32 && q.x_dtype != QMOE_BF16)
+      return fail(QMOE_ERR_UNSUPPORTED, "qgemv_batch: matrix %d unknown x_dtype %d", i, q.x_dtype);
+    if (work && (!QMOE_ALIGNED(q.W, 256) || !QMOE_ALIGNED(q.x, 16) || !QMOE_ALIGNED(q.y, 4)))
+      return fail(QMOE_ERR_INVALID_ARG, "qgemv_batch: matrix %d misaligned pointer", i);
+    P.d[i] = q;
+  }
+  int RC = 1;
+  size_t lds = 0, total_bytes = 0;
+  for (int i = 0; i < n; ++i)
+    if (d[i].N > 0 && d[i].R > 0) total_bytes += layout_of(d[i].fmt, d[i].N, d[i].K).total;
+  for (int i = 0; i < n; ++i) {
+    const qmoe_gemv_desc& q = d[i];
+    const int rc = pick_rc(q.R, q.K);
+    P.G[i] = lanes_per_row(q.K);
+    int tr = pick_tile_rows_bytes(q.N, P.G[i], layout_of(q.fmt, q.N, q.K).total, total_bytes);
+    const bool mc = q.R > rc;
+    P.rc[i] = mc ? 0 : rc;
+    any_mfma |= mc;
+    if (!mc) {
+      RC = std::max(RC, rc);
+      lds = std::max(lds, stage_bytes(rc, q.K));
+    } else {
+      lds = std::max(lds, mfma_red_bytes(1));
+    }
+    if (mc) {
+      const int pass = 16 * mfma_cols_per_pass(1);
+      tr = (tr + pass - 1) / pass * pass;
+    }
+    P.tile_rows[i] = tr;
+    P.block_off[i] = (int)blocks;
+    blocks += (q.N == 0 || q.R == 0) ? 0 : (q.N + tr - 1) / tr;
+  }
+  P.block_off[n] = (int)blocks;
+  if (blocks == 0) return QMOE_OK;
+  hipStream_t s = (hipStream_t)stream;
+  const dim3 grid((unsigned)blocks);
+  if (any_mfma)
+    return QMOE_LAUNCH("qgemv", (qgemv_batch_kernel<4, true>), grid, kBlock, lds, s, P);
+  if (RC == 1) return QMOE_LAUNCH("qgemv", (qgemv_batch_kernel<1, false>), grid, kBlock, lds, s, P);
+  if (RC == 2) return QMOE_LAUNCH("qgemv", (qgemv_batch_kernel<2, false>), grid, kBlock, lds, s, P);
+  return QMOE_LAUNCH("qgemv", (qgemv_batch_kernel<4, false>), grid, kBlock, lds, s, P);
 }
 
 template <int PHASE, bool MFMA>
@@ -995,6 +1144,10 @@ int qgemv_q4_k(const void* W, int N, int K, const void* x, int d, int R, float* 
 }
 int qgemv_q6_k(const void* W, int N, int K, const void* x, int d, int R, float* y, void* s) {
   return qgemv_launch(QMOE_Q6_K, W, N, K, x, d, R, y, s);
+}
+
+int qgemv_batch(const qmoe_gemv_desc* descs, int n, void* stream) {
+  return qgemv_batch_launch(descs, n, stream);
 }
 
 size_t moe_ffn_workspace_size(int T, int k, int F) {

@@ -179,9 +179,14 @@ class DenseLayer:
     def weight_bytes(self):
         return sum(qmoe.tensor_bytes(f, N, K) for (_, N, K, f) in self.cfg.mats)
 
-    def forward(self, x, copy=0):
-        outs = []
+    def forward(self, x, copy=0, batched=False):
+        """Every matrix against its input (x, or x[name] per matrix): one
+        qgemv launch per matrix, or all of them in one qgemv_batch launch
+        (the inputs are independent here)."""
+        items = []
         for i, (name, N, K, fmt) in enumerate(self.cfg.mats):
             xin = x[name] if isinstance(x, dict) else x
-            outs.append(qmoe.gemv(fmt, self.mats[copy][i], N, K, xin, out=self.out[i]))
-        return outs
+            items.append((fmt, self.mats[copy][i], N, K, xin, self.out[i]))
+        if batched:
+            return qmoe.gemv_batch(items)
+        return [qmoe.gemv(f, W, N, K, xin, out=o) for (f, W, N, K, xin, o) in items]

@@ -23,6 +23,15 @@ class QmoeError(RuntimeError):
     pass
 
 
+MAX_BATCH = 16
+
+
+class GemvDesc(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32),
+                ("x_dtype", ctypes.c_int32), ("R", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("W", ctypes.c_void_p), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p)]
+
+
 class Tier(ctypes.Structure):
     _fields_ = [("e_begin", ctypes.c_int32), ("e_end", ctypes.c_int32),
                 ("fmt_gate_up", ctypes.c_int32), ("fmt_down", ctypes.c_int32),
@@ -62,6 +71,7 @@ for _f in FORMATS:
     _SIGNATURES[f"qquantize_{_f}"] = (_I, [_VP, _I, _I, _VP, _VP])
     _SIGNATURES[f"qdequant_{_f}"] = (_I, [_VP, _I, _I, _VP, _VP])
     _SIGNATURES[f"qgemv_{_f}"] = (_I, [_VP, _I, _I, _VP, _I, _I, _VP, _VP])
+_SIGNATURES["qgemv_batch"] = (_I, [_VP, _I, _VP])
 
 
 def lib():
@@ -170,6 +180,27 @@ def dequantize(fmt, W, N, K, out=None):
         out = torch.empty((N, K), dtype=torch.float32, device=W.device)
     _check(getattr(lib(), f"qdequant_{fmt}")(_p(W), N, K, _p(out), _stream()), f"qdequant_{fmt}")
     return out
+
+
+def gemv_batch(items):
+    """One launch for several independent GEMVs.  items: (fmt, W, N, K, x, out)
+    tuples as gemv takes them (out required, [R, N] fp32); returns the outs."""
+    torch = _torch()
+    if len(items) > MAX_BATCH:
+        raise ValueError(f"at most {MAX_BATCH} matrices per batch")
+    descs = (GemvDesc * max(len(items), 1))()
+    keep = []
+    for i, (fmt, W, N, K, x, out) in enumerate(items):
+        x2 = x if x.dim() == 2 else x.reshape(1, -1)
+        _cuda_contig(W, x2, out)
+        _need(x2.shape[1] == K, "x has the wrong length")
+        _need(tuple(out.shape) == (x2.shape[0], N) and out.dtype == torch.float32,
+              "out must be fp32 [R, N]")
+        keep.append(x2)
+        descs[i] = GemvDesc(FORMATS[fmt], N, K, _dtype_code(x2), x2.shape[0], 0,
+                            _p(W), _p(x2), _p(out))
+    _check(lib().qgemv_batch(descs, len(items), _stream()), "qgemv_batch")
+    return [it[5] for it in items]
 
 
 def gemv(fmt, W, N, K, x, out=None):

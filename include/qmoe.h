@@ -131,9 +131,9 @@ int qmoe_device_cu_count(void);
  *   fp32.  R >= 0 (R rows share one pass over W).  Activations are rounded to
  *   fp16 inside the dot product: |x| must stay below 65504.  Up to 4 rows
  *   (fewer for long K) run as fp16 dot products against the exact codes; more
- *   rows, or K > 27456, run on the matrix cores, where each dequantized
- *   weight is also rounded to fp16 (relative 2^-11; magnitudes below 2^-14
- *   fall into fp16 subnormals).
+ *   rows, or K > 27456, run on the matrix cores, also against the exact codes
+ *   (the unit scale multiplies the fp32 result), so only the activations are
+ *   rounded.
  * Errors: INVALID_ARG for null pointers, N or K < 0, K % B != 0, K > 65536,
  *   misalignment; UNSUPPORTED for an unknown x_dtype.                      */
 #define QMOE_DECLARE_FORMAT(F)                                                 \
@@ -147,6 +147,25 @@ QMOE_DECLARE_FORMAT(mxfp4)
 QMOE_DECLARE_FORMAT(q4_k)
 QMOE_DECLARE_FORMAT(q6_k)
 #undef QMOE_DECLARE_FORMAT
+
+/* qgemv_batch: y_i = deq(W_i) x_i for n independent matrices in one launch
+ *   (the dense layer's matrices of [P3] section 4.4 streamed back to back
+ *   instead of one launch each).  descs[i] holds what qgemv_<fmt> takes for
+ *   matrix i (fmt one of QMOE_Q8_0 .. QMOE_Q6_K); every y_i equals that
+ *   qgemv call's result bit for bit.  No y_i may overlap any W_j, x_j or y_j.
+ *   descs is host memory, read during the call only.  A matrix with N == 0
+ *   or R == 0 is skipped (its pointers may be NULL).
+ * Limits: 0 <= n <= QMOE_MAX_BATCH; per matrix as qgemv, and R <= 16.
+ * Errors: as qgemv, for the first offending matrix; INVALID_ARG for n out of
+ *   range or null descs (n > 0).                                           */
+#define QMOE_MAX_BATCH 16
+typedef struct qmoe_gemv_desc {
+  int32_t fmt, N, K, x_dtype, R, reserved;
+  const void *W; /* device, 256-byte aligned, qmoe_tensor_bytes(fmt, N, K) */
+  const void *x; /* device [R, K] of x_dtype, 16-byte aligned */
+  float *y;      /* device [R, N] fp32 */
+} qmoe_gemv_desc;
+int qgemv_batch(const qmoe_gemv_desc *descs, int n, void *stream);
 
 /* ----------------------------------------------------------- routing ----
  * moe_route ([P2] "瓶颈分析": a light router picks the top-k of E experts per

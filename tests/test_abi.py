@@ -88,6 +88,16 @@ def test_host_validation_rejects_before_launch(L):
                               fake, fake, fake, fake, 1 << 30, None) == -2
     assert L.moe_route_decode(fake, 0, 1, 64, fake, None, 513, 8, 0, fake, fake, None,
                               fake, fake, fake, fake, 1 << 30, None) == -2
+    # batched GEMV: too many matrices, unknown format, bad K
+    from decode_moe_mul_amd import qmoe as qm
+    descs = (qm.GemvDesc * 17)()
+    assert L.qgemv_batch(descs, 17, None) == -1
+    assert L.qgemv_batch(None, 0, None) == 0
+    descs[0] = qm.GemvDesc(9, 8, 64, 0, 1, 0, 256 * 1000, 256 * 1000, 256 * 1000)
+    assert L.qgemv_batch(descs, 1, None) == -2
+    descs[0] = qm.GemvDesc(0, 8, 100, 0, 1, 0, 256 * 1000, 256 * 1000, 256 * 1000)
+    assert L.qgemv_batch(descs, 1, None) == -1
+    assert b"matrix 0" in L.qmoe_last_error()
     # permute: E too large
     assert L.moe_permute(fake, 4, 2, 9000, fake, fake, fake, None) == -2
     # combine: H not a multiple of 4

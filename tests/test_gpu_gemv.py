@@ -125,3 +125,38 @@ def test_llama8b_layer_shapes_sampled_rows():
         y_ref, bound = moe.gemv(fmt, buf, len(rows), K, x)
         assert_within_bound(y[:, rows], y_ref, bound, what=f"{name} {N}x{K}")
     assert layer.weight_bytes() == 137822208
+
+
+# ------------------------------------------------------------- batched ---
+
+def test_gemv_batch_equals_one_launch_per_matrix():
+    """qgemv_batch runs each matrix exactly as qgemv does: mixed formats,
+    shapes, dtypes and row counts (dot products, chunked rows, matrix cores,
+    a K too long for two staged rows) in one launch, outputs equal bit for
+    bit (qgemv's own parity with the oracle is tested above)."""
+    rng = np.random.default_rng(7)
+    cases = [("q4_k", 1000, 4096, 1, "f32"), ("q6_k", 640, 14336, 1, "f32"),
+             ("q8_0", 96, 640, 3, "bf16"), ("q4_0", 2048, 2048, 6, "f32"),
+             ("mxfp4", 33, 512, 16, "bf16"), ("q4_k", 64, 256, 2, "f32"),
+             ("q6_k", 17, 1024, 4, "bf16")]
+    items, singles = [], []
+    for i, (fmt, N, K, R, dt) in enumerate(cases):
+        w = synth.normal((N, K), 0.02, 30 + i, synth.DENSE)
+        W = qmoe.quantize(fmt, to_gpu(w))
+        x = synth.normal((R, K), 1.0, 40 + i, synth.ACT)
+        xg = to_gpu(x) if dt == "f32" else to_gpu(synth.bf16_round(x)).to(torch.bfloat16)
+        out = torch.full((R, N), float("nan"), dtype=torch.float32, device="cuda")
+        items.append((fmt, W, N, K, xg, out))
+        singles.append(qmoe.gemv(fmt, W, N, K, xg))
+    outs = qmoe.gemv_batch(items)
+    for (fmt, N, K, R, dt), a, b in zip(cases, outs, singles):
+        assert_bitexact(to_np(a), to_np(b), what=f"batch {fmt} N={N} K={K} R={R}")
+
+
+def test_gemv_batch_empty_and_zero_rows():
+    assert qmoe.gemv_batch([]) == []
+    W = qmoe.quantize("q8_0", to_gpu(synth.normal((8, 64), 0.02, 1, synth.DENSE)))
+    x = torch.zeros((0, 64), dtype=torch.float32, device="cuda")
+    out = torch.zeros((0, 8), dtype=torch.float32, device="cuda")
+    qmoe.gemv_batch([("q8_0", W, 8, 64, x, out)])
+    torch.cuda.synchronize()
