@@ -27,7 +27,7 @@ Timed passes (each over the same steps, inputs and weight rotation):
 Also reported: the fraction of the 8 TB/s HBM peak, the gate/up HBM traffic
 from stored counter runs, and the CPU oracle timed on a bounded sample.
 
-    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--no-cpu-baseline] [--decode-only]
 """
 import argparse
 import json
@@ -295,6 +295,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="skip the dense-GEMV and prefill sections (counter runs)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the traffic summary from two rocprofv3 --pmc runs and exit")
     a = ap.parse_args()
@@ -379,8 +381,8 @@ def main():
                  ("route_decode", "router_gemv", "topk", "permute", "ffn_gate_up", "ffn_down",
                   "combine")}
 
-    dense = dense_gemv(torch, a.steps)
-    prefill = prefill_chunk(torch)
+    dense = None if a.decode_only else dense_gemv(torch, a.steps)
+    prefill = None if a.decode_only else prefill_chunk(torch)
 
     t = stored_traffic()
     traffic = None if t is None else int(t["traffic_bytes_per_launch"])
@@ -419,8 +421,10 @@ def main():
                      "avg_launch_us": round(gu_ms * 1e3 / max(n_gu, 1), 3),
                      "algorithmic_bytes_per_launch": int(np.sum(gate_up_bytes) / max(n_gu, 1))},
     }
-    out["dense_gemv"] = dense
-    out["prefill"] = prefill
+    if dense is not None:
+        out["dense_gemv"] = dense
+    if prefill is not None:
+        out["prefill"] = prefill
     if not a.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         out["cpu_baseline"] = cpu_baseline()
