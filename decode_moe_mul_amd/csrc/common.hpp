@@ -84,6 +84,10 @@ QMOE_D float fdot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, a), __builtin_bit_cast(h2_t, b), c, false);
 }
 // 2^(e-127) for an E8M0 byte; 255 is NaN; e = 0 is the fp32 subnormal 2^-127
+// a * b + c with the 24-bit multiplier (a, b < 2^24; the result must fit in 32
+// bits): one full-rate v_mad_u32_u24 instead of a 32- or 64-bit multiply.
+QMOE_D uint32_t mad24(uint32_t a, uint32_t b, uint32_t c) { return __umul24(a, b) + c; }
+
 // Weight bytes are read once per call: the nontemporal hint streams them
 // past the caches instead of displacing lines that are reused.
 QMOE_D uint4 load_stream(const void* p) {

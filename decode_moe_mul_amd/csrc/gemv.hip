@@ -69,30 +69,33 @@ struct Unit {
   uint2 qh;      // Q6_K high bits
   uint32_t s0, s1;
 
+  // Offsets are 32-bit (a plane of one matrix is < 4 GiB) and products use
+  // the 24-bit multiplier (row < 65536, row strides <= 32 KiB), so a load
+  // costs a couple of vector instructions on top of the matrix's scalar base.
   QMOE_D void load(const Mat& M, int row, int u, int K) {
-    const size_t nb32 = (size_t)(K >> 5);
+    const uint32_t r = (uint32_t)row, uu = (uint32_t)u, nb32 = (uint32_t)(K >> 5);
     if constexpr (FMT == QMOE_Q8_0) {
-      const uint4* p = (const uint4*)(M.p0 + (size_t)row * K + 32 * (size_t)u);
-      q = load_stream(p);
-      q2 = load_stream(p + 1);
-      s0 = ((const uint16_t*)M.p1)[row * nb32 + u];
-    } else if constexpr (FMT == QMOE_Q4_0) {
-      q = load_stream(M.p0 + (size_t)row * (K >> 1) + 16 * (size_t)u);
-      s0 = ((const uint16_t*)M.p1)[row * nb32 + u];
-    } else if constexpr (FMT == QMOE_MXFP4) {
-      q = load_stream(M.p0 + (size_t)row * (K >> 1) + 16 * (size_t)u);
-      s0 = M.p1[row * nb32 + u];
-    } else if constexpr (FMT == QMOE_Q4_K) {
-      q = load_stream(M.p0 + (size_t)row * (K >> 1) + 16 * (size_t)u);
-      meta = ((const uint4*)M.p1)[(size_t)row * (K >> 8) + (u >> 3)];
+      const uint32_t qo = mad24(r, (uint32_t)K, uu << 5);
+      q = load_stream(M.p0 + qo);
+      q2 = load_stream(M.p0 + qo + 16u);
+      s0 = *(const uint16_t*)(M.p1 + (mad24(r, nb32, uu) << 1));
     } else {
-      q = load_stream(M.p0 + (size_t)row * (K >> 1) + 16 * (size_t)u);
-      qh = *(const uint2*)(M.p1 + (size_t)row * (K >> 2) + 8 * (size_t)u);
-      const size_t sb = (size_t)row * (K >> 8) + (u >> 3);
-      // the aligned word holding the unit's two sub-block scales (bytes
-      // 2j, 2j+1 of the super-block's 16, j = u & 7; picked at decode)
-      s0 = ((const uint32_t*)(M.p2 + 16 * sb))[(u & 7) >> 1];
-      s1 = ((const uint16_t*)M.p3)[sb];
+      const uint32_t qo = mad24(r, (uint32_t)(K >> 1), uu << 4);
+      q = load_stream(M.p0 + qo);
+      if constexpr (FMT == QMOE_Q4_0) {
+        s0 = *(const uint16_t*)(M.p1 + (mad24(r, nb32, uu) << 1));
+      } else if constexpr (FMT == QMOE_MXFP4) {
+        s0 = M.p1[mad24(r, nb32, uu)];
+      } else if constexpr (FMT == QMOE_Q4_K) {
+        meta = *(const uint4*)(M.p1 + (mad24(r, (uint32_t)(K >> 8), uu >> 3) << 4));
+      } else {
+        qh = *(const uint2*)(M.p1 + mad24(r, (uint32_t)(K >> 2), uu << 3));
+        const uint32_t sb = mad24(r, (uint32_t)(K >> 8), uu >> 3);
+        // the aligned word holding the unit's two sub-block scales (bytes
+        // 2j, 2j+1 of the super-block's 16, j = u & 7; picked at decode)
+        s0 = *(const uint32_t*)(M.p2 + (sb << 4) + ((uu & 6u) << 1));
+        s1 = *(const uint16_t*)(M.p3 + (sb << 1));
+      }
     }
   }
 
@@ -884,9 +887,16 @@ __global__ __launch_bounds__(kBlock, 2) void ffn_decode_kernel(FfnParams P) {
   __syncthreads();
   int tile = 0;
   bool big = false;
-  const int e = scheduled_expert(offs, E, m_max, blockIdx.x, ntiles, P.ntiles_big, red, tile, big);
+  // block-uniform values read from LDS, moved to scalar registers so that
+  // the weight bases derived from them stay scalar (loads then take a
+  // scalar base and a 32-bit vector offset)
+  const int e = __builtin_amdgcn_readfirstlane(
+      scheduled_expert(offs, E, m_max, blockIdx.x, ntiles, P.ntiles_big, red, tile, big));
   if (e < 0) return;
-  const int pos0 = offs[e], m = offs[e + 1] - offs[e];
+  tile = __builtin_amdgcn_readfirstlane(tile);
+  big = __builtin_amdgcn_readfirstlane((int)big) != 0;
+  const int pos0 = __builtin_amdgcn_readfirstlane(offs[e]);
+  const int m = __builtin_amdgcn_readfirstlane(offs[e + 1]) - pos0;
   qmoe_tier t;
   if (!tier_of(P.tiers, P.n_tiers, e, t)) return;
   const int fmt = PHASE == 0 ? t.fmt_gate_up : t.fmt_down;
