@@ -141,27 +141,27 @@ struct Unit {
   // The 8-value slice [8g, 8g + 8) of unit u for the matrix-core path:
   // q.x (Q8_0: q.x, q.y) holds its codes; scales as for the whole unit.
   QMOE_D void load_slice(const Mat& M, int row, int u, int g, int K) {
-    const size_t nb32 = (size_t)(K >> 5);
+    const uint32_t r = (uint32_t)row, uu = (uint32_t)u, gg = (uint32_t)g, nb32 = (uint32_t)(K >> 5);
     if constexpr (FMT == QMOE_Q8_0) {
-      const uint2 v = *(const uint2*)(M.p0 + (size_t)row * K + 32 * (size_t)u + 8 * g);
+      const uint2 v = *(const uint2*)(M.p0 + mad24(r, (uint32_t)K, (uu << 5) + (gg << 3)));
       q.x = v.x;
       q.y = v.y;
-      s0 = ((const uint16_t*)M.p1)[row * nb32 + u];
+      s0 = *(const uint16_t*)(M.p1 + (mad24(r, nb32, uu) << 1));
     } else {
-      q.x = *(const uint32_t*)(M.p0 + (size_t)row * (K >> 1) + 16 * (size_t)u + 4 * g);
+      q.x = *(const uint32_t*)(M.p0 + mad24(r, (uint32_t)(K >> 1), (uu << 4) + (gg << 2)));
       if constexpr (FMT == QMOE_Q4_0) {
-        s0 = ((const uint16_t*)M.p1)[row * nb32 + u];
+        s0 = *(const uint16_t*)(M.p1 + (mad24(r, nb32, uu) << 1));
       } else if constexpr (FMT == QMOE_MXFP4) {
-        s0 = M.p1[row * nb32 + u];
+        s0 = M.p1[mad24(r, nb32, uu)];
       } else if constexpr (FMT == QMOE_Q4_K) {
-        meta = ((const uint4*)M.p1)[(size_t)row * (K >> 8) + (u >> 3)];
+        meta = *(const uint4*)(M.p1 + (mad24(r, (uint32_t)(K >> 8), uu >> 3) << 4));
       } else {
         // high bits of values 8g..8g+7: bytes 2g, 2g + 1 of the unit's 8,
         // read as the aligned word holding them (half picked at decode)
-        qh.x = *(const uint32_t*)(M.p1 + (size_t)row * (K >> 2) + 8 * (size_t)u + 4 * (g >> 1));
-        const size_t sb = (size_t)row * (K >> 8) + (u >> 3);
-        s0 = ((const uint32_t*)(M.p2 + 16 * sb))[(u & 7) >> 1];
-        s1 = ((const uint16_t*)M.p3)[sb];
+        qh.x = *(const uint32_t*)(M.p1 + mad24(r, (uint32_t)(K >> 2), (uu << 3) + ((gg >> 1) << 2)));
+        const uint32_t sb = mad24(r, (uint32_t)(K >> 8), uu >> 3);
+        s0 = *(const uint32_t*)(M.p2 + (sb << 4) + ((uu & 6u) << 1));
+        s1 = *(const uint16_t*)(M.p3 + (sb << 1));
       }
     }
   }
@@ -872,7 +872,7 @@ QMOE_D int scheduled_expert(const int* offs, int E, int m_max, int b, int ntiles
 // experts with more than m_max rows can occur (the matrix-core branch costs
 // registers, so launches that cannot use it leave it out).
 template <int PHASE, int RC, bool MFMA>
-__global__ __launch_bounds__(kBlock, 2) void ffn_decode_kernel(FfnParams P) {
+__global__ __launch_bounds__(kBlock, (PHASE == 1 || RC <= 2) ? 3 : 2) void ffn_decode_kernel(FfnParams P) {
   extern __shared__ __align__(16) uint8_t smem[];
   // scalars used below, read once from the argument block
   const int E = P.E, H = P.H, F = P.F, kk = P.k, dtype = P.x_dtype, m_max = P.m_max;
