@@ -36,7 +36,7 @@ extern "C" int moe_permute(const int32_t* ids, int T, int k, int E, int32_t* off
   if (A > 0 && (!ids || !perm || !inv_perm))
     return fail(QMOE_ERR_INVALID_ARG, "moe_permute: null pointer");
   // waves: as many as the LDS table [W][E] allows, up to 16
-  const int W = permute_waves(E, kPermLds, kPermBlock / 64);
+  const int W = permute_waves(A, E, kPermLds, kPermBlock / 64);
   return QMOE_LAUNCH("permute", permute_kernel, dim3(1), kPermBlock, 0, (hipStream_t)stream,
                      ids, (int)A, E, W, id_bits(E), offsets, perm, inv_perm);
 }

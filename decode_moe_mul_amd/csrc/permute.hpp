@@ -106,10 +106,14 @@ QMOE_D void permute_block(const int32_t* ids, int A, int E, int W, int nbits, in
   for (long long i = (long long)total + threadIdx.x; i < A; i += NT) perm[i] = -1;
 }
 
-// waves of a permute_block over E experts with `lds_ints` ints of LDS for hist
-QMOE_HD int permute_waves(int E, int lds_ints, int max_waves) {
+// waves of a permute_block over A assignments and E experts with `lds_ints`
+// ints of LDS for hist: one per 64 assignments (more would only add empty
+// histograms to clear and scan), at most max_waves and what the LDS holds
+QMOE_HD int permute_waves(long long A, int E, int lds_ints, int max_waves) {
   int W = lds_ints / E;
   if (W > max_waves) W = max_waves;
+  const long long by_a = (A + 63) / 64;
+  if (W > by_a) W = (int)by_a;
   return W < 1 ? 1 : W;
 }
 QMOE_HD int id_bits(int E) {

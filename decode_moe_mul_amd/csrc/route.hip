@@ -565,7 +565,7 @@ int moe_route_decode(const void* x, int x_dtype, int T, int H, const float* Wr,
   D.perm = perm;
   D.inv = inv_perm;
   D.E_total = E_total;
-  D.W = permute_waves(E_total, hist_ints, kGemvBlock / 64);
+  D.W = permute_waves(A, E_total, hist_ints, kGemvBlock / 64);
   D.nbits = id_bits(E_total);
   const dim3 grid((E + kGemvExperts - 1) / kGemvExperts, D.r.KS);
   const size_t lds = (size_t)kDecodeLdsInts * 4;
