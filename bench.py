@@ -273,7 +273,7 @@ def prefill_chunk(torch, calls=10):
     _events_ms(torch, lambda i: layer.forward(x, i % 2, prefill=True), calls)
     qmoe.profile_enable(False)
     kern = {k: qmoe.profile_read(k)[1] / calls for k in
-            ("router_gemm", "topk", "permute", "prefill_schedule", "prefill_gate_up",
+            ("router_gemm", "topk", "permute", "prefill_prep", "prefill_gate_up",
              "prefill_down", "combine")}
     gemm_ms = kern["prefill_gate_up"] + kern["prefill_down"]
     del layer

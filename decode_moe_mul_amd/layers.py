@@ -106,7 +106,7 @@ class MoELayer:
                 "inv": torch.empty(max(A, 1), dtype=torch.int32, device=dev),
                 "o": torch.empty((max(A, 1), c.H), dtype=torch.float32, device=dev),
                 "y": torch.empty((T, c.H), dtype=torch.float32, device=dev),
-                "ffn": (qmoe.prefill_workspace(T, kt, c.E_total, c.F, dev) if prefill
+                "ffn": (qmoe.prefill_workspace(T, kt, c.E_total, c.H, c.F, dev) if prefill
                         else qmoe.ffn_workspace(T, kt, c.F, dev)),
             }
             self._ws[key] = ws

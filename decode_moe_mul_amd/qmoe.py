@@ -57,7 +57,7 @@ _SIGNATURES = {
     "moe_ffn_workspace_size": (_SZ, [_I, _I, _I]),
     "moe_ffn_tiered": (_I, [ctypes.POINTER(Tier), _I, _I, _I, _I, _VP, _I, _I, _I, _VP, _VP,
                             _VP, _VP, _SZ, _VP]),
-    "qgemm_grouped_prefill_workspace_size": (_SZ, [_I, _I, _I, _I]),
+    "qgemm_grouped_prefill_workspace_size": (_SZ, [_I, _I, _I, _I, _I]),
     "qgemm_grouped_prefill": (_I, [ctypes.POINTER(Tier), _I, _I, _I, _I, _VP, _I, _I, _I, _VP,
                                    _VP, _VP, _VP, _SZ, _VP]),
     "moe_combine": (_I, [_VP, _VP, _VP, _I, _I, _I, _VP, _VP, _VP]),
@@ -305,8 +305,8 @@ def ffn_workspace(T, k, F, device="cuda"):
     return _alloc_bytes(lib().moe_ffn_workspace_size(T, k, F), device)
 
 
-def prefill_workspace(T, k, E, F, device="cuda"):
-    return _alloc_bytes(lib().qgemm_grouped_prefill_workspace_size(T, k, E, F), device)
+def prefill_workspace(T, k, E, H, F, device="cuda"):
+    return _alloc_bytes(lib().qgemm_grouped_prefill_workspace_size(T, k, E, H, F), device)
 
 
 def _ffn_call(name, tiers, E, H, F, x, k, offsets, perm, out, ws):
@@ -332,7 +332,7 @@ def ffn_tiered(tiers, E, H, F, x, k, offsets, perm, out=None, ws=None):
 def grouped_prefill(tiers, E, H, F, x, k, offsets, perm, out=None, ws=None):
     """o [T*k, H] in permuted order (matrix-core grouped GEMM)."""
     if ws is None:
-        ws = prefill_workspace(x.shape[0], k, E, F, x.device)
+        ws = prefill_workspace(x.shape[0], k, E, H, F, x.device)
     return _ffn_call("qgemm_grouped_prefill", tiers, E, H, F, x, k, offsets, perm, out, ws)
 
 

@@ -252,11 +252,16 @@ int moe_ffn_tiered(const qmoe_tier *tiers, int n_tiers, int E, int H, int F,
 
 /* qgemm_grouped_prefill: the same result as moe_ffn_tiered for long chunks
  * (a 2048-token prefill chunk, [P4] "120 t/s 的秘密微批次分组解码"): per
- * expert, weight tiles are dequantized to bf16 and multiplied on the matrix
- * cores with fp32 accumulation; activations are rounded to bf16 and h is
- * stored as bf16 between the two passes.  Same arguments as moe_ffn_tiered.
- * Workspace: qgemm_grouped_prefill_workspace_size(T, k, E, F) bytes.        */
-size_t qgemm_grouped_prefill_workspace_size(int T, int k, int E, int F);
+ * expert, rows are cut into tiles of 128; each tile's weights are
+ * dequantized to fp16 in registers (the exact code times its block scale,
+ * rounded once) and multiplied on the matrix cores against the tile's
+ * activations with fp32 accumulation ([P1] section 九.3).  x is rounded to
+ * fp16 once (|x| must stay below 65504) and h = SiLU(g) * u is stored as
+ * fp16 between the gate/up pass and the down pass.  Same arguments as
+ * moe_ffn_tiered; H and F must be multiples of 64.
+ * Workspace: qgemm_grouped_prefill_workspace_size(T, k, E, H, F) bytes:
+ * h [T*k, F] fp16, x [T, H] fp16 and the tile table.                        */
+size_t qgemm_grouped_prefill_workspace_size(int T, int k, int E, int H, int F);
 int qgemm_grouped_prefill(const qmoe_tier *tiers, int n_tiers, int E, int H,
                           int F, const void *x, int x_dtype, int T, int k,
                           const int32_t *offsets, const int32_t *perm, float *o,

@@ -201,11 +201,9 @@ def test_empty_and_zero_token_calls():
 
 # -------------------------------------------------------------- prefill ---
 
-# The prefill path rounds x, the dequantized weights and h to bf16 (2^-9).  Its
-# error relative to sum|w x| falls like 1/sqrt(K); at the workload's K (H 2048,
-# F 640) it sits several standard deviations inside 1e-3, at K = 64 it does
-# not.  These layers keep the workload's reduction lengths (or longer) with
-# fewer experts.
+# The prefill path rounds x, the dequantized weights and h to fp16 (2^-11).  Its
+# error relative to sum|w x| falls like 1/sqrt(K), so these layers keep
+# reduction lengths of several hundred values or more with fewer experts.
 PREFILL_TIERED = MoEConfig("prefill_tiered_small", H=2048, E=24, k=6, F=640,
                            tiers=(Tier(0, 6, "q6_k", "q8_0"), Tier(6, 19, "q4_k", "q4_0"),
                                   Tier(19, 24, "mxfp4", "mxfp4")), rows=(300,),
@@ -213,9 +211,17 @@ PREFILL_TIERED = MoEConfig("prefill_tiered_small", H=2048, E=24, k=6, F=640,
 PREFILL_SHARED = MoEConfig("prefill_shared_small", H=1024, E=16, k=4, F=1024,
                            tiers=(Tier(0, 16, "q4_k", "q4_k"),), rows=(200,), x_dtype="bf16",
                            n_shared=1, shared_fmt="q8_0")
+# ragged everywhere: H = 34 units of 32 and F = 10 units (K steps of 4 units
+# end short in both passes), H not a multiple of the 128-column down tile,
+# experts with more rows than one 128-row tile
+PREFILL_RAGGED = MoEConfig("prefill_ragged", H=1088, E=10, k=3, F=320,
+                           tiers=(Tier(0, 4, "q8_0", "q8_0"), Tier(4, 8, "q4_0", "q4_0"),
+                                  Tier(8, 10, "mxfp4", "mxfp4")), rows=(260,),
+                           prior_lambda=0.5)
 
 
-@pytest.mark.parametrize("cfg,T", [(PREFILL_TIERED, 300), (PREFILL_SHARED, 200)])
+@pytest.mark.parametrize("cfg,T", [(PREFILL_TIERED, 300), (PREFILL_SHARED, 200),
+                                   (PREFILL_RAGGED, 260)])
 def test_prefill_small_layers(cfg, T):
     _check_layer(cfg, T, prefill=True)
 
