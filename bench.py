@@ -25,7 +25,9 @@ Timed passes (each over the same steps, inputs and weight rotation):
      roofline of the dominant kernel (ffn_gate_up);
   4. events around every launch: kernel_ms_per_step (context only).
 Also reported: the fraction of the 8 TB/s HBM peak, the gate/up HBM traffic
-from stored counter runs, and the CPU oracle timed on a bounded sample.
+from stored counter runs, and the CPU oracle timed on a bounded sample; and,
+outside the step, the dense layer GEMV (Llama-3-8B shapes, Q4_K/Q6_K and the
+ternary T5 format) and the 2048-row prefill chunk.
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--no-cpu-baseline] [--decode-only]
 """
@@ -249,6 +251,44 @@ def dense_gemv(torch, steps):
     return res
 
 
+def ternary_gemv(torch, steps):
+    """The same layer's seven matrices in the ternary T5 format (1.75 bits per
+    weight), one fp32 row, 8 weight copies rotated: one qgemv_t5 launch per
+    matrix, and all seven in one qgemv_batch launch."""
+    from decode_moe_mul_amd import configs, layers, synth
+    from decode_moe_mul_amd import qmoe
+    cfg = configs.LLAMA8B_GEMV_T5
+    layer = layers.DenseLayer(cfg, copies=8)
+    x = torch.from_numpy(synth.normal((1, 4096), 1.0, 3, synth.ACT, 0)).cuda()
+    xd = torch.from_numpy(synth.normal((1, 14336), 1.0, 3, synth.ACT, 1)).cuda()
+    xs = {n: (xd if n == "down" else x) for (n, _, _, _) in cfg.mats}
+    nbytes = layer.weight_bytes()
+    nweights = sum(N * K for (_, N, K, _) in cfg.mats)
+    res = {"workload": "llama3_8b_layer_gemv T5 ternary x7 (1.75 bits/weight), 1 fp32 row",
+           "weight_bytes": int(nbytes)}
+    for mode, batched in (("per_matrix", False), ("batched", True)):
+        fwd = lambda i: layer.forward(xs, i % 8, batched=batched)
+        for i in range(16):
+            fwd(i)
+        ms = _events_ms(torch, fwd, steps)
+        qmoe.profile_reset()
+        qmoe.profile_enable(True)
+        _events_ms(torch, fwd, steps)
+        qmoe.profile_enable(False)
+        kernel_ms = qmoe.profile_read("qgemv_t5")[1] / steps
+        log(f"ternary layer gemv ({mode}): {ms * 1e3:.1f} us per token "
+            f"({kernel_ms * 1e3:.1f} us in kernels)")
+        res[mode] = {"us_per_token": round(ms * 1e3, 2),
+                     "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                     "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "kernel_us": round(kernel_ms * 1e3, 2),
+                     "kernel_gbs": round(nbytes / (kernel_ms * 1e-3) / 1e9, 1),
+                     "gweights_per_s": round(nweights / (ms * 1e-3) / 1e9, 1)}
+    del layer
+    torch.cuda.empty_cache()
+    return res
+
+
 def prefill_chunk(torch, calls=10):
     """The tiered 512-expert layer on a 2048-row prefill chunk: router GEMM,
     top-k, permutation, grouped gate/up and down on the matrix cores, combine.
@@ -383,6 +423,7 @@ def main():
                   "combine")}
 
     dense = None if a.decode_only else dense_gemv(torch, a.steps)
+    ternary = None if a.decode_only else ternary_gemv(torch, a.steps)
     prefill = None if a.decode_only else prefill_chunk(torch)
 
     t = stored_traffic()
@@ -424,6 +465,8 @@ def main():
     }
     if dense is not None:
         out["dense_gemv"] = dense
+    if ternary is not None:
+        out["ternary_gemv"] = ternary
     if prefill is not None:
         out["prefill"] = prefill
     if not a.no_cpu_baseline:

@@ -86,6 +86,11 @@ LLAMA8B_GEMV = DenseConfig("llama3_8b_layer_gemv", mats=(
     ("gate", 14336, 4096, "q4_k"), ("up", 14336, 4096, "q4_k"),
     ("down", 4096, 14336, "q6_k")))
 
+# the same layer's matrices in the ternary T5 format (1.75 bits per weight,
+# "RTX 4080 SUPER native Windows 27B: NInfer 80 SM port" page, section 九.2)
+LLAMA8B_GEMV_T5 = DenseConfig("llama3_8b_layer_gemv_t5", mats=tuple(
+    (name, N, K, "t5") for (name, N, K, _) in LLAMA8B_GEMV.mats))
+
 TIERED_TIERS = (Tier(0, 128, "q6_k", "q8_0"),
                 Tier(128, 410, "q4_k", "q4_0"),
                 Tier(410, 512, "mxfp4", "mxfp4"))

@@ -99,8 +99,9 @@ int validate_tiers(const qmoe_tier* tiers, int n_tiers, int E, int H, int F, boo
     if (t.e_begin < 0 || t.e_end > E || t.e_begin >= t.e_end)
       return fail(QMOE_ERR_INVALID_ARG, "%s: tier %d range [%d,%d) outside [0,%d)", who, i,
                   t.e_begin, t.e_end, E);
-    if (block_of(t.fmt_gate_up) == 0 || block_of(t.fmt_down) == 0)
-      return fail(QMOE_ERR_UNSUPPORTED, "%s: tier %d unknown format", who, i);
+    if (!tier_format(t.fmt_gate_up) || !tier_format(t.fmt_down))
+      return fail(QMOE_ERR_UNSUPPORTED, "%s: tier %d: format not one of the tier formats", who,
+                  i);
     if (H % block_of(t.fmt_gate_up) || F % block_of(t.fmt_down) || F % 32)
       return fail(QMOE_ERR_INVALID_ARG, "%s: tier %d: H=%d / F=%d not multiples of the blocks",
                   who, i, H, F);

@@ -29,8 +29,15 @@ QMOE_HD size_t round_up256(size_t n) { return (n + 255) & ~size_t(255); }
 QMOE_HD int block_of(int fmt) {
   return (fmt == QMOE_Q4_K || fmt == QMOE_Q6_K) ? 256
          : (fmt >= QMOE_Q8_0 && fmt <= QMOE_MXFP4) ? 32
+         : fmt == QMOE_T5                           ? 128
                                                   : 0;
 }
+
+// The formats of the routed-expert tiers (the ternary T5 is a dense-GEMV format).
+QMOE_HD bool tier_format(int fmt) { return fmt >= QMOE_Q8_0 && fmt <= QMOE_Q6_K; }
+
+// T5: 28-byte groups of 128 weights (26 base-3 code bytes, then fp16 d).
+constexpr int kT5GroupBytes = 28;
 
 // Plane sizes per format, in storage order, for a [N, K] tensor.
 QMOE_HD Layout layout_of(int fmt, int N, int K) {
@@ -46,6 +53,7 @@ QMOE_HD Layout layout_of(int fmt, int N, int K) {
     case QMOE_Q6_K:
       sz[0] = n * k / 2; sz[1] = n * k / 4; sz[2] = n * (k / 256) * 16;
       sz[3] = n * (k / 256) * 2; np = 4; break;
+    case QMOE_T5: sz[0] = n * (k / 128) * kT5GroupBytes; np = 1; break;
     default: np = 0;
   }
   size_t pos = 0;

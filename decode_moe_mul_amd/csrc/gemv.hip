@@ -27,6 +27,7 @@
 //  * Gate and up rows of the same output are handled by the same lanes, so
 //    SiLU(g) * u is applied in registers before anything is stored.
 #include <algorithm>
+#include <cstdio>
 
 #include "common.hpp"
 #include "dequant.hpp"
@@ -947,6 +948,9 @@ __global__ __launch_bounds__(kBlock, (PHASE == 1 || RC <= 2) ? 3 : 2) void ffn_d
 }
 
 // ------------------------------------------------------ host helpers ----
+int t5_check(const char* who, const qmoe_gemv_desc& q);             // ternary.hip
+int t5_batch_launch(const qmoe_gemv_desc* d, int n, void* stream);  // ternary.hip
+
 // Lanes per weight row: the largest power of two <= 64 dividing the unit
 // count K/32 that still leaves every lane >= 4 units.
 static int lanes_per_row(int K) {
@@ -1057,13 +1061,26 @@ static int qgemv_batch_launch(const qmoe_gemv_desc* d, int n, void* stream) {
     return fail(QMOE_ERR_INVALID_ARG, "qgemv_batch: n=%d outside [0, %d]", n, QMOE_MAX_BATCH);
   if (n == 0) return QMOE_OK;
   if (!d) return fail(QMOE_ERR_INVALID_ARG, "qgemv_batch: null descriptors");
+  int n_t5 = 0;
+  for (int i = 0; i < n; ++i) n_t5 += d[i].fmt == QMOE_T5;
+  if (n_t5 == n) {  // a batch of ternary matrices: the T5 kernel
+    for (int i = 0; i < n; ++i) {
+      char who[32];
+      snprintf(who, sizeof who, "qgemv_batch: matrix %d", i);
+      const int st = t5_check(who, d[i]);
+      if (st) return st;
+    }
+    return t5_batch_launch(d, n, stream);
+  }
   GemvBatchParams P{};
   P.n = n;
   bool any_mfma = false;
   long long blocks = 0;
   for (int i = 0; i < n; ++i) {
     const qmoe_gemv_desc& q = d[i];
-    if (!block_of(q.fmt)) return fail(QMOE_ERR_UNSUPPORTED, "qgemv_batch: matrix %d unknown format", i);
+    if (!tier_format(q.fmt))  // (T5 only in batches of T5 matrices)
+      return fail(QMOE_ERR_UNSUPPORTED, "qgemv_batch: matrix %d: format %d not in this batch", i,
+                  q.fmt);
     const bool work = q.N > 0 && q.R > 0;  // empty products touch no memory
     if (work && (!q.W || !q.x || !q.y))
       return fail(QMOE_ERR_INVALID_ARG, "qgemv_batch: matrix %d null pointer", i);

@@ -61,6 +61,56 @@ QMOE_D uint32_t e2m1_code(double m) {
   return 7;
 }
 
+// T5: one thread per 128-group.  d = fp16(mean |w|) (the float64 sum of the
+// group's |w| divided by 128), t = clamp(round(w / d), -1, 1) against the
+// stored d; code byte b = sum over r < 5 of (t + 1) * 3^r for weights 5b + r
+// (t = 0 past weight 127); bytes 26, 27 = d.
+__global__ __launch_bounds__(256) void quantize_t5_kernel(const float* w, int N, int K,
+                                                          uint8_t* out) {
+  const int nb = K / 128;
+  const size_t blk = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (blk >= (size_t)N * nb) return;
+  const size_t n = blk / nb, b = blk - n * nb;
+  const float* src = w + n * K + b * 128;
+  double sum = 0.0;
+  for (int i = 0; i < 128; ++i) sum += fabs((double)src[i]);
+  const uint32_t d16 = f64_to_f16_rne(sum / 128.0);
+  const double d = f16_bits_to_f64(d16);
+  uint8_t* g = out + blk * kT5GroupBytes;
+  for (int j = 0; j < 26; ++j) {
+    uint32_t code = 0, pw = 1;
+    for (int r = 0; r < 5; ++r) {
+      const int i = 5 * j + r;
+      const int t = i < 128 ? (int)clampd(round_half_away(safe_div((double)src[i], d)), -1, 1) : 0;
+      code += (uint32_t)(t + 1) * pw;
+      pw *= 3;
+    }
+    g[j] = (uint8_t)code;
+  }
+  g[26] = (uint8_t)d16;
+  g[27] = (uint8_t)(d16 >> 8);
+}
+
+// T5 reference decoder: one thread per 32 values (d * t is exact in fp32).
+__global__ __launch_bounds__(256) void dequant_t5_kernel(const uint8_t* W, int N, int K,
+                                                         float* out) {
+  const int U = K / 32;
+  const size_t id = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (id >= (size_t)N * U) return;
+  const size_t n = id / U, u = id - n * U;
+  const uint8_t* g = W + (n * (K / 128) + u / 4) * kT5GroupBytes;
+  const float d = f16_bits_to_f32(g[26] | (g[27] << 8));
+  float v[32];
+  for (int i = 0; i < 32; ++i) {
+    const int e = 32 * (int)(u & 3) + i;  // weight index within the group
+    int c = g[e / 5];
+    for (int r = 0; r < e % 5; ++r) c /= 3;
+    v[i] = d * (float)(c % 3 - 1);
+  }
+  float4* dst = (float4*)(out + n * K + 32 * u);
+  for (int i = 0; i < 8; ++i) dst[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+}
+
 // One thread per block of B values.
 template <int FMT>
 __global__ __launch_bounds__(256) void quantize_kernel(const float* w, int N, int K, uint8_t* out) {
@@ -254,8 +304,12 @@ static int quantize_launch(const float* w, int N, int K, void* out, void* stream
   if (!QMOE_ALIGNED(out, 256)) return fail(QMOE_ERR_INVALID_ARG, "qquantize: misaligned out");
   if (N == 0) return QMOE_OK;
   const size_t nblk = (size_t)N * (K / block_of(FMT));
-  return QMOE_LAUNCH("quantize", quantize_kernel<FMT>, dim3((unsigned)((nblk + 255) / 256)), 256,
-                     0, (hipStream_t)stream, w, N, K, (uint8_t*)out);
+  if constexpr (FMT == QMOE_T5)
+    return QMOE_LAUNCH("quantize", quantize_t5_kernel, dim3((unsigned)((nblk + 255) / 256)), 256,
+                       0, (hipStream_t)stream, w, N, K, (uint8_t*)out);
+  else
+    return QMOE_LAUNCH("quantize", quantize_kernel<FMT>, dim3((unsigned)((nblk + 255) / 256)),
+                       256, 0, (hipStream_t)stream, w, N, K, (uint8_t*)out);
 }
 
 template <int FMT>
@@ -266,8 +320,12 @@ static int dequant_launch(const void* W, int N, int K, float* out, void* stream)
     return fail(QMOE_ERR_INVALID_ARG, "qdequant: misaligned pointer");
   if (N == 0) return QMOE_OK;
   const size_t nu = (size_t)N * (K / 32);
-  return QMOE_LAUNCH("dequant", dequant_kernel<FMT>, dim3((unsigned)((nu + 255) / 256)), 256, 0,
-                     (hipStream_t)stream, (const uint8_t*)W, N, K, out);
+  if constexpr (FMT == QMOE_T5)
+    return QMOE_LAUNCH("dequant", dequant_t5_kernel, dim3((unsigned)((nu + 255) / 256)), 256, 0,
+                       (hipStream_t)stream, (const uint8_t*)W, N, K, out);
+  else
+    return QMOE_LAUNCH("dequant", dequant_kernel<FMT>, dim3((unsigned)((nu + 255) / 256)), 256,
+                       0, (hipStream_t)stream, (const uint8_t*)W, N, K, out);
 }
 
 }  // namespace qmoe
@@ -286,3 +344,4 @@ QMOE_DEFINE_FORMAT(q4_0, QMOE_Q4_0)
 QMOE_DEFINE_FORMAT(mxfp4, QMOE_MXFP4)
 QMOE_DEFINE_FORMAT(q4_k, QMOE_Q4_K)
 QMOE_DEFINE_FORMAT(q6_k, QMOE_Q6_K)
+QMOE_DEFINE_FORMAT(t5, QMOE_T5)

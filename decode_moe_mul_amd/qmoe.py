@@ -12,7 +12,7 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libqmoe.so")
 
-FORMATS = {"q8_0": 0, "q4_0": 1, "mxfp4": 2, "q4_k": 3, "q6_k": 4}
+FORMATS = {"q8_0": 0, "q4_0": 1, "mxfp4": 2, "q4_k": 3, "q6_k": 4, "t5": 5}
 F32, BF16 = 0, 1
 MAX_TIERS = 8
 

@@ -56,6 +56,13 @@
  *                 sub-blocks).                             value d*sc_j*q - dmin*m_j
  *   Q6_K  B=256 : ql 4-bit[256]; qh 2-bit[256]; sc int8[16]; d fp16 (16-value
  *                 sub-blocks).                             value d*sc_j*(q-32)
+ *   T5    B=128 : one plane of 28-byte groups: 26 base-3 code bytes, then
+ *                 fp16 d.  Weight i of a group is digit i mod 5 (least
+ *                 significant first) of code byte i div 5, holding t + 1;
+ *                 byte 25 holds weights 125..127 (digits 3, 4 are t = 0).
+ *                 1.75 bits per weight.                    value d*t, t in {-1,0,1}
+ *                 ("t5_g128_fp16" of [P1] section 九.2: base-3, five weights
+ *                 per byte, one FP16 scale per 128 weights.)
  *   4-bit element i of a row: byte i>>1, low nibble for even i.  Q6_K high
  *   bits of element i: byte i>>2, bits 2*(i&3).  E2M1: bit3 sign, bits 2-1
  *   exponent, bit 0 mantissa, magnitudes {0,.5,1,1.5,2,3,4,6} (OCP MX v1.0).
@@ -86,7 +93,8 @@ typedef enum {
   QMOE_Q4_0 = 1,
   QMOE_MXFP4 = 2,
   QMOE_Q4_K = 3,
-  QMOE_Q6_K = 4
+  QMOE_Q6_K = 4,
+  QMOE_T5 = 5 /* ternary, dense GEMV only (not a tier format) */
 } qmoe_format;
 
 typedef enum { QMOE_F32 = 0, QMOE_BF16 = 1 } qmoe_dtype;
@@ -97,7 +105,7 @@ const char *qmoe_status_string(int status);
 /* Detail text of the calling thread's most recent failing call ("" if none). */
 const char *qmoe_last_error(void);
 /* Block size B of a format (32 or 256), or 0 for an unknown format. */
-int qmoe_block_size(int fmt);
+int qmoe_block_size(int fmt);  /* 128 for QMOE_T5 */
 /* Bytes of a packed [N, K] tensor; 0 if fmt is unknown or K % B != 0. */
 size_t qmoe_tensor_bytes(int fmt, int N, int K);
 /* Byte offset of each plane of a packed [N, K] tensor (up to 4 planes).
@@ -123,6 +131,7 @@ int qmoe_device_cu_count(void);
  *            q = clamp(round((w + dmin*m)/(d*sc)), 0, 15)
  *     Q6_K : per 16-sub-block s = max|w|/31; d = fp16(max s/127),
  *            sc = clamp(round(s/d),-128,127), q = clamp(round(w/(d*sc))+32,0,63)
+ *     T5   : per 128-group d = fp16(mean|w|), t = clamp(round(w/d), -1, 1)
  *   (the offline per-tier packing of [P2] "优化策略二", done on the device).
  * qdequant_<fmt>: packed [N, K] -> out [N, K] fp32, each value the exact
  *   format value rounded to nearest-even fp32 (bit-exact reference decoder).
@@ -147,6 +156,19 @@ QMOE_DECLARE_FORMAT(mxfp4)
 QMOE_DECLARE_FORMAT(q4_k)
 QMOE_DECLARE_FORMAT(q6_k)
 #undef QMOE_DECLARE_FORMAT
+/* T5 (ternary): qquantize_t5, qdequant_t5 as above.  qgemv_t5 as qgemv_<fmt>
+ *   with 1 <= R <= 16: code bytes are decoded to ternary fp16 pairs in
+ *   registers and dotted with fp16-rounded activations (|x| < 65504), so the
+ *   products are exact and only the activations are rounded.  Code bytes
+ *   above 242 are not produced by qquantize_t5 and give unspecified values.
+ *   ([P1] section 九.2: ternary decode is memory-bound.)
+ * Limits: K <= 20096 (one staged activation row fits in LDS; UNSUPPORTED
+ *   beyond).
+ * Errors: as qgemv_<fmt>; INVALID_ARG for K % 128 != 0 or R > 16.          */
+int qquantize_t5(const float *w, int N, int K, void *out, void *stream);
+int qdequant_t5(const void *W, int N, int K, float *out, void *stream);
+int qgemv_t5(const void *W, int N, int K, const void *x, int x_dtype, int R,
+             float *y, void *stream);
 
 /* qgemv_batch: y_i = deq(W_i) x_i for n independent matrices in one launch
  *   (the dense layer's matrices of [P3] section 4.4 streamed back to back

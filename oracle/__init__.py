@@ -8,8 +8,8 @@ package never imports the product.
 Everything here is a plain, slow, obviously correct restatement of what the
 path computes, in float64 NumPy:
 
-* ``oracle.formats``  -- the five block formats: quantizer, packer, unpacker,
-  exact dequantization (Q8_0, Q4_0, MXFP4, Q4_K, Q6_K).
+* ``oracle.formats``  -- the block formats: quantizer, packer, unpacker,
+  exact dequantization (Q8_0, Q4_0, MXFP4, Q4_K, Q6_K and the ternary T5).
 * ``oracle.moe``      -- dense quantized GEMV, router + softmax top-k,
   expert permutation, expert FFN with SwiGLU, weighted combine, the whole
   routed-expert layer, and the per-element error bounds used for parity.

@@ -58,6 +58,12 @@ def element(fmt, buf, N, K, n, k):
         sc = sc - 256 if sc > 127 else sc
         d = _f16(buf[offs[3] + 2 * blk], buf[offs[3] + 2 * blk + 1])
         return d * sc * ((lo | (hi << 4)) - 32)
+    if fmt == "t5":
+        g = offs[0] + fm.T5_GROUP_BYTES * blk
+        i = k % 128
+        code = buf[g + i // 5]
+        digit = (code // 3 ** (i % 5)) % 3
+        return _f16(buf[g + 26], buf[g + 27]) * (digit - 1)
     raise ValueError(fmt)
 
 

@@ -34,6 +34,17 @@ those formats; the byte arrangement ("planes") is this project's own:
                plane 2: sc int8 x16
                plane 3: d  fp16; sub-block j is elements 16j..16j+15
 
+  T5    B=128  plane 0: 28-byte groups: bytes 0..25 base-3 codes, bytes 26..27
+               fp16 d                  value d*t, t in {-1, 0, +1}
+               (the "t5_g128_fp16" ternary format of the "RTX 4080 SUPER
+               native Windows 27B: NInfer 80 SM port" page, section 九.2:
+               base-3, five weights per byte, one FP16 scale per 128
+               weights, 1.75 bits per weight.)  Weight i of a group is digit
+               i mod 5 (least significant first) of code byte i div 5; a
+               digit holds t + 1.  Byte 25 holds weights 125..127 in digits
+               0..2 and t = 0 in digits 3..4.  26 + 2 bytes per 128 weights
+               is exactly the page's 1.75 bits per weight.
+
   4-bit packing: element i of a row lives in byte i>>1 of the row's plane
   slice, low nibble for even i.  Q6_K high bits: element i lives in byte i>>2,
   bits 2*(i&3)..2*(i&3)+1.  E2M1 code: bit 3 sign, bits 2-1 exponent, bit 0
@@ -41,6 +52,8 @@ those formats; the byte arrangement ("planes") is this project's own:
   Formats specification v1.0, FP4 E2M1 element type).  E8M0 code 255 is NaN.
 
 Quantizer readings (the pages give none; the Q8_0 rule is the workload's):
+  * T5: d = fp16(mean |w|) over the group, t = clamp(round(w/d), -1, 1)
+    (the absolute-mean scale of ternary weight quantization);
   * all arithmetic in float64 on the float32 input values;
   * scales are rounded to fp16 round-to-nearest-even, and codes are computed
     against the *stored* fp16 scale;
@@ -50,10 +63,13 @@ Quantizer readings (the pages give none; the Q8_0 rule is the workload's):
 import numpy as np
 
 FORMATS = ("q8_0", "q4_0", "mxfp4", "q4_k", "q6_k")
-BLOCK = {"q8_0": 32, "q4_0": 32, "mxfp4": 32, "q4_k": 256, "q6_k": 256}
+# the ternary format has its own tests (it is not a tier format of the layer)
+TERNARY = ("t5",)
+BLOCK = {"q8_0": 32, "q4_0": 32, "mxfp4": 32, "q4_k": 256, "q6_k": 256, "t5": 128}
 # bits per weight of the densely packed form (planes add only alignment)
 BITS_PER_WEIGHT = {"q8_0": 8.5, "q4_0": 4.5, "mxfp4": 4.25, "q4_k": 4.5,
-                   "q6_k": 6.5625}
+                   "q6_k": 6.5625, "t5": 1.75}
+T5_GROUP_BYTES = 28   # 26 code bytes + fp16 d
 E2M1_MAGNITUDE = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
 
 
@@ -79,6 +95,8 @@ def plane_bytes(fmt, N, K):
         return [N * K // 2, N * nb * 16]
     if fmt == "q6_k":
         return [N * K // 2, N * K // 4, N * nb * 16, N * nb * 2]
+    if fmt == "t5":
+        return [N * nb * T5_GROUP_BYTES]
     raise ValueError(fmt)
 
 
@@ -225,9 +243,18 @@ def quantize_q6_k(W):
             "sc": sc.astype(np.int8)}
 
 
+def quantize_t5(W):
+    """Ternary: per 128-group d = fp16(mean |w|), t = clamp(round(w/d), -1, 1)
+    against the stored d (zero divisor: t = 0)."""
+    b, N, K = _as_blocks(W, 128)
+    d16 = fp16_rne(np.abs(b).mean(axis=2))
+    t = np.clip(round_half_away(_safe_div(b, d16.astype(np.float64)[..., None])), -1, 1)
+    return {"t": t.astype(np.int8).reshape(N, K), "d": d16}
+
+
 QUANTIZE = {"q8_0": quantize_q8_0, "q4_0": quantize_q4_0,
             "mxfp4": quantize_mxfp4, "q4_k": quantize_q4_k,
-            "q6_k": quantize_q6_k}
+            "q6_k": quantize_q6_k, "t5": quantize_t5}
 
 
 # ------------------------------------------------------------- packing -----
@@ -277,6 +304,16 @@ def pack(fmt, fields, N, K):
         planes = [_pack_nibbles(fields["q"]),
                   _pack_q4k_meta(fields["d"], fields["dmin"], fields["sc"],
                                  fields["m"])]
+    elif fmt == "t5":
+        nb = K // 128
+        c = fields["t"].astype(np.int64).reshape(N, nb, 128) + 1          # digits 0..2
+        c = np.concatenate([c, np.ones((N, nb, 2), dtype=np.int64)], axis=2)  # pad t = 0
+        c = c.reshape(N, nb, 26, 5)
+        codes = (c * np.array([1, 3, 9, 27, 81], dtype=np.int64)).sum(axis=3)
+        grp = np.zeros((N, nb, T5_GROUP_BYTES), dtype=np.uint8)
+        grp[..., :26] = codes.astype(np.uint8)
+        grp[..., 26:28] = fields["d"].astype("<f2").view(np.uint8).reshape(N, nb, 2)
+        planes = [grp]
     elif fmt == "q6_k":
         q = fields["q"].reshape(N, K)
         hi = (q >> 4) & 3
@@ -355,6 +392,15 @@ def unpack(fmt, buf, N, K):
         m = np.stack([field(48 + 6 * j) for j in range(8)], -1)
         return {"q": _nibble(p[0], N, K), "d": d, "dmin": dmin,
                 "sc": sc.astype(np.int64), "m": m.astype(np.int64)}
+    if fmt == "t5":
+        grp = p[0].reshape(N, nb, T5_GROUP_BYTES)
+        code = grp[..., :26].astype(np.int64)
+        digits = np.empty((N, nb, 26, 5), dtype=np.int64)
+        for r in range(5):
+            digits[..., r] = code % 3
+            code = code // 3
+        t = digits.reshape(N, nb, 130)[..., :128] - 1
+        return {"t": t.reshape(N, K), "d": grp[..., 26:28].copy().view("<f2")[..., 0].astype(np.float64)}
     if fmt == "q6_k":
         lo = _nibble(p[0], N, K)
         qh = p[1].reshape(N, K // 4).astype(np.int64)
@@ -398,6 +444,8 @@ def dequantize(fmt, buf, N, K):
         d = per_block(f["d"])
         sc = np.repeat(f["sc"].reshape(N, -1), 16, axis=1)
         return d * sc * (f["q"] - 32)
+    if fmt == "t5":
+        return per_block(f["d"]) * f["t"]
     raise ValueError(fmt)
 
 

@@ -144,3 +144,32 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(qmoe, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(qmoe.QmoeError):
         qmoe.lib()
+
+
+def test_t5_ternary_entry_points_and_limits(L):
+    """The ternary format's layout queries and host-side checks (no launch)."""
+    from decode_moe_mul_amd import qmoe
+    T5 = qmoe.FORMATS["t5"]
+    fake = ctypes.c_void_p(256 * 1000)
+    assert L.qmoe_block_size(T5) == 128
+    for N, K in [(1, 128), (3, 384), (4096, 4096), (640, 2048)]:
+        assert L.qmoe_tensor_bytes(T5, N, K) == fm.tensor_bytes("t5", N, K)
+    assert L.qmoe_tensor_bytes(T5, 4, 100) == 0
+    assert L.qgemv_t5(fake, 4, 100, fake, 0, 1, fake, None) == -1     # K % 128
+    assert L.qgemv_t5(fake, 4, 256, fake, 0, 17, fake, None) == -1    # R > 16
+    assert L.qgemv_t5(fake, 4, 20224, fake, 0, 1, fake, None) == -2   # staged row > LDS
+    assert L.qgemv_t5(fake, 0, 256, fake, 0, 1, fake, None) == 0      # no rows: no-op
+    # T5 is not a tier format
+    tier = qmoe.Tier(0, 8, T5, 0, 256000, 256000, 256000)
+    arr = (qmoe.Tier * 1)(tier)
+    ws_need = L.moe_ffn_workspace_size(2, 2, 256)
+    assert L.moe_ffn_tiered(arr, 1, 8, 256, 256, fake, 0, 2, 2, fake, fake, fake, fake,
+                            ws_need, None) == -2
+    # qgemv_batch takes batches of T5 matrices (checked as qgemv_t5 checks)
+    # but not T5 mixed with other formats
+    descs = (qmoe.GemvDesc * 2)(qmoe.GemvDesc(T5, 8, 256, 0, 1, 0, 256000, 256000, 256000),
+                                qmoe.GemvDesc(T5, 8, 100, 0, 1, 0, 256000, 256000, 256000))
+    assert L.qgemv_batch(descs, 2, None) == -1
+    assert b"matrix 1" in L.qmoe_last_error()
+    descs[1] = qmoe.GemvDesc(3, 8, 256, 0, 1, 0, 256000, 256000, 256000)
+    assert L.qgemv_batch(descs, 2, None) == -2
