@@ -25,16 +25,24 @@ def _torch():
 
 
 class MoELayer:
-    def __init__(self, cfg, seed=None, device="cuda", copies=1):
+    def __init__(self, cfg, seed=None, device="cuda", copies=1, order=None):
+        """order: optional re-indexing of the routed experts (new id ->
+        original id, as a tier plan makes): routed expert e of this layer is
+        the synthetic expert order[e], with its router row and logit bias."""
         torch = _torch()
         self.cfg = cfg
         self.seed = cfg.seed if seed is None else seed
         self.device = device
         H, E, F = cfg.H, cfg.E, cfg.F
-        self.Wr = synth.normal_device((E, H), cfg.sigma_router, self.seed, synth.ROUTER, 0, device)
+        self.order = np.arange(E) if order is None else np.asarray(order, dtype=np.int64)
+        if sorted(self.order.tolist()) != list(range(E)):
+            raise ValueError("order must be a permutation of the routed expert ids")
+        idx = torch.as_tensor(self.order, device=device)
+        self.Wr = synth.normal_device((E, H), cfg.sigma_router, self.seed, synth.ROUTER, 0,
+                                      device)[idx].contiguous()
         self.bias = None
         if cfg.prior_lambda is not None:
-            self.bias = torch.from_numpy(synth.rank_prior(E, cfg.prior_lambda)).to(device)
+            self.bias = torch.from_numpy(synth.rank_prior(E, cfg.prior_lambda)).to(device)[idx].contiguous()
         self.tiers = cfg.all_tiers()
         banks = []
         for t in self.tiers:
@@ -61,7 +69,7 @@ class MoELayer:
     # ----------------------------------------------------------- weights --
     def _keys(self, e):
         if e < self.cfg.E:
-            return (synth.GATE, synth.UP, synth.DOWN), e
+            return (synth.GATE, synth.UP, synth.DOWN), int(self.order[e])
         return (synth.SH_GATE, synth.SH_UP, synth.SH_DOWN), e - self.cfg.E
 
     def expert_fp32_device(self, e):
