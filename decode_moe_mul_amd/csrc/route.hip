@@ -13,162 +13,13 @@
 //  topk_kernel         one wave per row: sums the split-K partials in fixed
 //                      order, adds the bias, selects k by repeated wave
 //                      arg-max, softmax over the kept logits.
-#include "permute.hpp"
+#include "route.hpp"
 
 namespace qmoe {
 
-constexpr int kRouteBlock = 256;
-constexpr int kGemvRowsMax = 16;
-// split-K router for <= 16 rows: 16 waves, one expert row of Wr per wave, so
-// that each staged x slice serves 16 experts
-constexpr int kGemvBlock = 1024;
-constexpr int kGemvExperts = kGemvBlock / 64;
-
-struct RouteParams {
-  const void* x;
-  int x_dtype, T, H;
-  const float* Wr;
-  const float* bias;
-  int E, k, n_shared;
-  int32_t* ids;
-  float* p;
-  float* logits;
-  float* part;  // [KS][T][E]
-  int KS, ks_len;
-};
-
-// 4 consecutive activations (fp32 or bf16) starting at element i (i % 4 == 0)
-template <int DT>
-QMOE_D float4 load_act4(const void* x, size_t i) {
-  if constexpr (DT == QMOE_F32) {
-    return *(const float4*)((const float*)x + i);
-  } else {
-    const uint2 b = *(const uint2*)((const uint16_t*)x + i);
-    return make_float4(bf16_bits_to_f32(b.x & 0xFFFFu), bf16_bits_to_f32(b.x >> 16),
-                       bf16_bits_to_f32(b.y & 0xFFFFu), bf16_bits_to_f32(b.y >> 16));
-  }
-}
-
-// x[:, k0:k0+len] -> xsl [T][ks_len], float4 granules, 4 loads in flight
-template <int DT, int NT>
-QMOE_D void stage_x_slice(const RouteParams& P, int k0, int len, float* xsl) {
-  const int l4 = len >> 2, n4 = P.T * l4;
-  for (int i0 = threadIdx.x; i0 < n4; i0 += 4 * NT) {
-    float4 v[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = min(i0 + u * NT, n4 - 1);  // unconditional loads
-      const int t = i / l4, j = 4 * (i - t * l4);
-      v[u] = load_act4<DT>(P.x, (size_t)t * P.H + k0 + j);
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = i0 + u * NT;
-      if (i < n4) {
-        const int t = i / l4, j = 4 * (i - t * l4);
-        *(float4*)(xsl + t * P.ks_len + j) = v[u];
-      }
-    }
-  }
-}
-
-// Device-coherent scalar access for values handed between blocks of one
-// launch: agent-scope relaxed atomics, i.e. stores written through and loads
-// served past the per-XCD L2, so that no cache-wide write-back or invalidate
-// (what a device fence costs) is needed.
-QMOE_D void store_coherent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-QMOE_D float load_coherent(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// This thread's outstanding vector-memory operations have completed (its
-// written-through stores are visible device-wide) before it goes on.
-QMOE_D void drain_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// Sum over the wave of acc[r] for 16 rows at once: each exchange step halves
-// the rows a lane carries (xor 32, 16, 8, 4), then xor 2 and 1 finish the
-// sums.  17 lane exchanges instead of 16 separate 6-step reductions.  Lane L
-// ends with the total of row ((L>>5)&1)*8 + ((L>>4)&1)*4 + ((L>>3)&1)*2 + ((L>>2)&1).
-QMOE_D float wave_sum16(float (&acc)[kGemvRowsMax]) {
-  const int lane = threadIdx.x & 63;
-  float a8[8], a4[4], a2[2];
-  const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8, b2 = lane & 4;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const float keep = b5 ? acc[8 + j] : acc[j], give = b5 ? acc[j] : acc[8 + j];
-    a8[j] = keep + __shfl_xor(give, 32, 64);
-  }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float keep = b4 ? a8[4 + j] : a8[j], give = b4 ? a8[j] : a8[4 + j];
-    a4[j] = keep + __shfl_xor(give, 16, 64);
-  }
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const float keep = b3 ? a4[2 + j] : a4[j], give = b3 ? a4[j] : a4[2 + j];
-    a2[j] = keep + __shfl_xor(give, 8, 64);
-  }
-  float v = (b2 ? a2[1] : a2[0]) + __shfl_xor(b2 ? a2[0] : a2[1], 4, 64);
-  v += __shfl_xor(v, 2, 64);
-  v += __shfl_xor(v, 1, 64);
-  return v;
-}
-
-// Block (b, ks) of the split-K router: wave w handles expert 16b+w over values
-// [ks*ks_len, (ks+1)*ks_len) of the hidden dimension (ks_len <= 1024, a
-// multiple of 256) and writes its partial dot products for all T rows to
-// part[ks][t][e] (written through when COH).  The weight row is requested
-// before x is staged, so both loads are in flight together.  Every thread
-// returns (no early exit), so callers may synchronise afterwards.
-template <bool COH>
-QMOE_D void router_partials(const RouteParams& P, float* xsl) {
-  const int ks = blockIdx.y;
-  const int k0 = ks * P.ks_len;
-  const int len = min(P.ks_len, P.H - k0);
-  const int lane = threadIdx.x & 63;
-  const int e = blockIdx.x * kGemvExperts + (threadIdx.x >> 6);
-  const bool has_e = e < P.E;
-  const float* wrow = P.Wr + (size_t)min(e, P.E - 1) * P.H + k0;
-  float4 w[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int j = 4 * lane + 256 * u;
-    w[u] = j < len ? *(const float4*)(wrow + j) : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-  if (P.x_dtype == QMOE_F32)
-    stage_x_slice<QMOE_F32, kGemvBlock>(P, k0, len, xsl);
-  else
-    stage_x_slice<QMOE_BF16, kGemvBlock>(P, k0, len, xsl);
-  __syncthreads();
-  float acc[kGemvRowsMax];
-#pragma unroll
-  for (int t = 0; t < kGemvRowsMax; ++t) {
-    acc[t] = 0.f;
-    if (t < P.T) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int j = 4 * lane + 256 * u;
-        if (j < len) {
-          const float4 xv = *(const float4*)(xsl + t * P.ks_len + j);
-          acc[t] += w[u].x * xv.x + w[u].y * xv.y + w[u].z * xv.z + w[u].w * xv.w;
-        }
-      }
-    }
-  }
-  const float v = wave_sum16(acc);
-  const int t = ((lane >> 5) & 1) * 8 + ((lane >> 4) & 1) * 4 + ((lane >> 3) & 1) * 2 +
-                ((lane >> 2) & 1);
-  if (has_e && (lane & 3) == 0 && t < P.T) {
-    float* dst = P.part + ((size_t)ks * P.T + t) * P.E + e;
-    if constexpr (COH) store_coherent(dst, v);
-    else *dst = v;
-  }
-}
-
 __global__ __launch_bounds__(kGemvBlock) void router_gemv_kernel(RouteParams P) {
   extern __shared__ __align__(16) float xsl[];  // [T][ks_len]
-  router_partials<false>(P, xsl);
+  router_partials<false, kGemvBlock>(P, xsl, blockIdx.x, blockIdx.y);
 }
 
 // 64 x 64 tile of logits (rows x experts) on the matrix cores in fp32
@@ -250,65 +101,6 @@ __global__ __launch_bounds__(kRouteBlock) void router_gemm_kernel(RouteParams P)
       }
 }
 
-// Order-preserving unsigned image of a logit (NaN ranks as -inf); every
-// number maps above 0, which marks taken / absent slots.
-QMOE_D uint32_t order_key(float f) {
-  if (f != f) f = -INFINITY;
-  const uint32_t b = __builtin_bit_cast(uint32_t, f);
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-}
-
-// Top-k of one row of E logits held by one wave (lane l holds experts
-// l + 64 i in raw[i]): k rounds of a wave arg-max (DPP max of the keys, then
-// DPP min of the ids that hold it, so ties go to the lower id).  Lane s < k
-// gets the s-th id and its logit.
-template <int PER>  // E <= 64 * PER
-QMOE_D void wave_topk(const float (&raw)[PER], int E, int k, int& my_id, float& my_raw) {
-  const int lane = threadIdx.x & 63;
-  uint32_t key[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) key[i] = lane + 64 * i < E ? order_key(raw[i]) : 0u;
-  my_id = 0;
-  my_raw = 0.f;
-  for (int s = 0; s < k; ++s) {
-    uint32_t kb = 0u, ib = 0xFFFFFFFFu;
-    float rb = 0.f;
-#pragma unroll
-    for (int i = 0; i < PER; ++i)  // ascending ids, strict: lowest id on ties
-      if (key[i] > kb) { kb = key[i]; ib = (uint32_t)(lane + 64 * i); rb = raw[i]; }
-    const uint32_t kmax = wave_max_u32(kb);
-    const uint32_t wid = wave_min_u32(kb == kmax ? ib : 0xFFFFFFFFu);
-    const float rsel = __builtin_bit_cast(
-        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rb), (int)(wid & 63u)));
-    if ((int)(wid & 63u) == lane) {
-#pragma unroll
-      for (int i = 0; i < PER; ++i)
-        if (i == (int)(wid >> 6)) key[i] = 0u;
-    }
-    if (lane == s) { my_id = (int)wid; my_raw = rsel; }
-  }
-}
-
-// ids/p of row t from its top-k (softmax over the kept logits relative to
-// the largest), shared experts appended with weight 1
-QMOE_D void write_topk(const RouteParams& P, int t, int my_id, float my_raw, int32_t* ids_copy) {
-  const int lane = threadIdx.x & 63;
-  const int kt = P.k + P.n_shared;
-  const float l0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_raw), 0));
-  const float w = lane < P.k ? expf(my_raw - l0) : 0.f;
-  float sum = w;
-  for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
-  if (lane < P.k) {
-    P.ids[(size_t)t * kt + lane] = my_id;
-    P.p[(size_t)t * kt + lane] = w / sum;
-    if (ids_copy) ids_copy[t * kt + lane] = my_id;
-  }
-  for (int s = lane; s < P.n_shared; s += 64) {
-    P.ids[(size_t)t * kt + P.k + s] = P.E + s;
-    P.p[(size_t)t * kt + P.k + s] = 1.f;
-    if (ids_copy) ids_copy[t * kt + P.k + s] = P.E + s;
-  }
-}
 
 // Final logits of row t, expert e: split-K partials summed in order + bias.
 QMOE_D float final_logit(const RouteParams& P, int t, int e) {
@@ -380,45 +172,12 @@ struct RouteDecodeParams {
 
 constexpr int kDecodeLdsInts = 8192;  // LDS ints of the fused kernel (32 KiB)
 
-// Final logits of row t for the lane's experts e = lane + 64 i: the KS
-// partials summed in slice order, then the bias (final_logit's order, so the
-// values equal moe_route's bit for bit).  Up to 32 loads per lane in flight;
-// row and slice offsets are wave-uniform (scalar), expert offsets per lane.
-template <int PER>
-QMOE_D void row_logits(const RouteParams& P, int t, float (&v)[PER]) {
-  constexpr int SC = PER >= 16 ? 1 : 32 / PER;  // K-slices per batch of loads
-  const int lane = threadIdx.x & 63;
-  const float* rowp = P.part + (size_t)t * P.E;
-  const size_t slice = (size_t)P.T * P.E;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) v[i] = 0.f;
-  for (int s0 = 0; s0 < P.KS; s0 += SC) {
-    float pv[SC][PER];
-#pragma unroll
-    for (int u = 0; u < SC; ++u) {
-      const float* sp = rowp + (size_t)min(s0 + u, P.KS - 1) * slice;
-#pragma unroll
-      for (int i = 0; i < PER; ++i)
-        pv[u][i] = load_coherent(sp + (uint32_t)min(lane + 64 * i, P.E - 1));
-    }
-#pragma unroll
-    for (int u = 0; u < SC; ++u)
-#pragma unroll
-      for (int i = 0; i < PER; ++i)
-        if (s0 + u < P.KS) v[i] += pv[u][i];
-  }
-  if (P.bias) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) v[i] += P.bias[min(lane + 64 * i, P.E - 1)];
-  }
-}
-
 template <int PER>
 __global__ __launch_bounds__(kGemvBlock) void route_decode_kernel(RouteDecodeParams D) {
   extern __shared__ __align__(16) float smem[];
   __shared__ int last;
   const RouteParams& P = D.r;
-  router_partials<true>(P, smem);
+  router_partials<true, kGemvBlock>(P, smem, blockIdx.x, blockIdx.y);
   drain_vmem();
   __syncthreads();
   if (threadIdx.x == 0)
@@ -448,14 +207,6 @@ __global__ __launch_bounds__(kGemvBlock) void route_decode_kernel(RouteDecodePar
                              hist + D.W * D.E_total);
   if (threadIdx.x == 0)
     __hip_atomic_store(&D.ctr[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-static void route_split(int T, int H, int& KS, int& ks_len) {
-  if (T > kGemvRowsMax) { KS = 1; ks_len = H; return; }
-  // K-slices of 1024 values (multiple of 256), capped so T*ks_len*4 <= 32 KiB
-  ks_len = 1024;
-  while (ks_len > 256 && (size_t)T * ks_len * 4 > 32768) ks_len /= 2;
-  KS = (H + ks_len - 1) / ks_len;
 }
 
 }  // namespace qmoe
