@@ -23,7 +23,9 @@ Timed passes (each over the same steps, inputs and weight rotation):
   2. each row count alone: tokens_per_s, ms_per_call;
   3. the library's HIP events around every gate/up launch only: the
      roofline of the dominant kernel (ffn_gate_up);
-  4. events around every launch: kernel_ms_per_step (context only).
+  4. events around every launch: kernel_ms_per_step (context only);
+  5. the 1- and 6-row calls as one cooperative launch each
+     (moe_layer_decode): one_launch_layer (context only).
 Also reported: the fraction of the 8 TB/s HBM peak, the gate/up HBM traffic
 from stored counter runs, and the CPU oracle timed on a bounded sample; and,
 outside the step, the dense layer GEMV (Llama-3-8B shapes, Q4_K/Q6_K and the
@@ -383,15 +385,19 @@ def main():
             layer.forward(x, copy)
     torch.cuda.synchronize()
 
-    def timed(calls_of_step, tag):
+    def timed(calls_of_step, tag, one_launch=False):
         """ms for a.steps steps of the given calls, events only at the ends."""
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
+        if one_launch:
+            for s in range(3):
+                for layer, x, copy, rows in calls_of_step(s):
+                    layer.forward(x, copy, one_launch=True)
         torch.cuda.synchronize()
         t0.record(stream)
         for s in range(a.steps):
             for layer, x, copy, rows in calls_of_step(s):
-                layer.forward(x, copy)
+                layer.forward(x, copy, one_launch=one_launch)
         t1.record(stream)
         torch.cuda.synchronize()
         log(f"timed {tag}: {t0.elapsed_time(t1) / a.steps:.4f} ms per step")
@@ -421,6 +427,16 @@ def main():
     kernel_ms = {k: qmoe.profile_read(k) for k in
                  ("route_decode", "router_gemv", "topk", "permute", "ffn_gate_up", "ffn_down",
                   "combine")}
+
+    # 5. the same 1- and 6-row calls as one cooperative launch each
+    #    (moe_layer_decode), same inputs and weight rotation
+    one_ms = np.array([timed(lambda s, i=i: [step_calls(tiered, grouped, xt, xg, s)[i]],
+                             f"one launch rows={r}", one_launch=True)
+                       for i, r in enumerate((1, 6))])
+    one_launch = {"ms_per_call": {str(r): round(one_ms[i] / a.steps, 5)
+                                  for i, r in enumerate((1, 6))},
+                  "tokens_per_s": {str(r): round(r * a.steps / (one_ms[i] * 1e-3), 1)
+                                   for i, r in enumerate((1, 6))}}
 
     dense = None if a.decode_only else dense_gemv(torch, a.steps)
     ternary = None if a.decode_only else ternary_gemv(torch, a.steps)
@@ -467,6 +483,7 @@ def main():
         out["dense_gemv"] = dense
     if ternary is not None:
         out["ternary_gemv"] = ternary
+    out["one_launch_layer"] = one_launch
     if prefill is not None:
         out["prefill"] = prefill
     if not a.no_cpu_baseline:

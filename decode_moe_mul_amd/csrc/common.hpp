@@ -281,6 +281,21 @@ QMOE_HD bool pair_up4(int p) {
   return (FMT == QMOE_Q4_0 || FMT == QMOE_Q4_K || FMT == QMOE_Q6_K) && (p & 1);
 }
 
+// ------------------------------------ hand-over between blocks ------
+// Device-coherent scalar access for values handed between blocks of one
+// launch: agent-scope relaxed atomics, i.e. stores written through and loads
+// served past the per-XCD L2, so that no cache-wide write-back or invalidate
+// (what a device fence costs) is needed.
+QMOE_D void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+QMOE_D float load_coherent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// This thread's outstanding vector-memory operations have completed (its
+// written-through stores are visible device-wide) before it goes on.
+QMOE_D void drain_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // ------------------------------------------------- wave reductions ------
 // Wave-wide max / min of unsigned values through DPP row shifts and row
 // broadcasts (lanes whose source is out of range keep the identity); the

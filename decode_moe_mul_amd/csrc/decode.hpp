@@ -216,9 +216,18 @@ QMOE_D float unit_dot(const uint32_t codes[16], float c0, float c1, const uint32
 QMOE_HD int tok_stride(int U) { return 64 * U + 16 * ((U + 3) >> 2); }
 QMOE_HD int unit_off(int u) { return 64 * u + 16 * (u >> 2); }
 
+// Activation rows written earlier in the same launch by other blocks are read
+// with coherent loads (COH, or XDT = kF32Coherent): fp32, past the L2.
+constexpr int kF32Coherent = 0x100;
+
 // 32 activation values (fp32 or raw bf16) starting at element 32u of row.
+template <bool COH = false>
 QMOE_D void load32(const void* row, int dtype, int u, float v[32]) {
-  if (dtype == QMOE_F32) {
+  if constexpr (COH) {
+    const float* p = (const float*)row + 32 * u;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = load_coherent(p + i);
+  } else if (dtype == QMOE_F32) {
     const float4* p = (const float4*)((const float*)row + 32 * u);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -248,13 +257,13 @@ QMOE_D void load32(const void* row, int dtype, int u, float v[32]) {
 //   Q4_0: {1024 S + 8 X, 0}          Q4_K: {1024 S, X}  (X meets the min)
 //   Q6_K: {1024 S + 32 X} over elements 0..15 and over 16..31
 //   Q8_0: {1152 S, 0}                MXFP4: {0, 0}
-template <int FMT, class Src>
+template <int FMT, bool COH = false, class Src>
 QMOE_D void stage_rows(uint8_t* xs, float2* sb, int rc, int U, Src src, int dtype) {
   const int ts = tok_stride(U);
   for (int idx = threadIdx.x; idx < rc * U; idx += kBlock) {
     const int r = idx / U, u = idx - r * U;
     float v[32];
-    load32(src(r), dtype, u, v);
+    load32<COH>(src(r), dtype, u, v);
     uint32_t w[16];
     float S[2] = {0.f, 0.f}, X[2] = {0.f, 0.f};
 #pragma unroll
@@ -401,7 +410,7 @@ QMOE_D void valu_pass(const Mat (&mats)[NMAT], int K, int rb, int re, int G, int
 
 // Stage up to `chunk` (<= RC) rows at a time and stream the tile against
 // them.
-template <int FMT, int NMAT, int RC, class SrcOf, class SinkOf>
+template <int FMT, int NMAT, int RC, bool COH = false, class SrcOf, class SinkOf>
 QMOE_D void valu_rows(const Mat (&mats)[NMAT], int K, int rb, int re, int G, int rows_total,
                       int dtype, uint8_t* lds, SrcOf src_of, SinkOf sink_of, int chunk = RC) {
   const int U = K >> 5;
@@ -410,7 +419,7 @@ QMOE_D void valu_rows(const Mat (&mats)[NMAT], int K, int rb, int re, int G, int
   for (int c0 = 0; c0 < rows_total; c0 += chunk) {
     const int rc = min(chunk, rows_total - c0);
     __syncthreads();
-    stage_rows<FMT>(xs, sb, rc, U, [&](int r) { return src_of(c0 + r); }, dtype);
+    stage_rows<FMT, COH>(xs, sb, rc, U, [&](int r) { return src_of(c0 + r); }, dtype);
     __syncthreads();
     // the register blocking of the pass follows this chunk's row count, so
     // an expert with one row does not pay for the dots of RC rows
@@ -477,6 +486,13 @@ QMOE_D void xslice_load(const void* row, int u, int g, XRaw8& x) {
     const uint4* p = (const uint4*)((const float*)row + 32 * u + 8 * g);
     x.a = p[0];
     x.b = p[1];
+  } else if constexpr (XDT == kF32Coherent) {
+    const float* p = (const float*)row + 32 * u + 8 * g;
+    uint32_t w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = __builtin_bit_cast(uint32_t, load_coherent(p + i));
+    x.a = make_uint4(w[0], w[1], w[2], w[3]);
+    x.b = make_uint4(w[4], w[5], w[6], w[7]);
   } else {
     x.a = *(const uint4*)((const uint16_t*)row + 32 * u + 8 * g);
   }
@@ -486,7 +502,7 @@ QMOE_D void xslice_load(const void* row, int u, int g, XRaw8& x) {
 template <int FMT, int XDT>
 QMOE_D void xslice_pairs(const XRaw8& x, bool valid, uint32_t out[4]) {
   float v[8];
-  if constexpr (XDT == QMOE_F32) {
+  if constexpr (XDT == QMOE_F32 || XDT == kF32Coherent) {
     const uint32_t w[8] = {x.a.x, x.a.y, x.a.z, x.a.w, x.b.x, x.b.y, x.b.z, x.b.w};
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = __builtin_bit_cast(float, w[i]);
@@ -758,6 +774,75 @@ QMOE_D int scheduled_expert(const int* offs, int E, int m_max, int b, int ntiles
   }
   __syncthreads();
   return red[2 * kWaves];
+}
+
+// One work item of the routed FFN: row tile `tile` of expert e, whose rows
+// are positions pos0 .. pos0 + m - 1 of the permutation (perm_of(pos) gives
+// the flat assignment t * k + i).  PHASE 0: gate/up + SwiGLU -> h;
+// PHASE 1: down -> o.  COH: h and o are handed to other blocks of the same
+// launch, so they are written through and h is read past the L2.
+template <int PHASE, int RC, bool MFMA, bool COH, class PermOf>
+QMOE_D void ffn_item(const FfnParams& P, int e, int tile, bool big, int pos0, int m,
+                     uint8_t* smem, PermOf perm_of) {
+  const int H = P.H, F = P.F, kk = P.k, dtype = P.x_dtype, G = P.G, tile_rows = P.tile_rows;
+  const char* xb = (const char*)P.x;
+  float* hbuf = P.h;
+  float* obuf = P.o;
+  qmoe_tier t;
+  if (!tier_of(P.tiers, P.n_tiers, e, t)) return;
+  const int fmt = PHASE == 0 ? t.fmt_gate_up : t.fmt_down;
+  const int N = PHASE == 0 ? F : H, K = PHASE == 0 ? H : F;
+  // few-row experts: weight rows [rb, re) of a row tile; many-row experts:
+  // a slice of whole matrix-core passes, N split over at most
+  // ntiles_big blocks
+  const int pass = 16 * mfma_cols_per_pass(PHASE == 0 ? 2 : 1);
+  const int cpt = ((N + P.ntiles_big - 1) / P.ntiles_big + pass - 1) / pass * pass;
+  const int rb = big ? tile * cpt : tile * tile_rows;
+  const int re = min(N, rb + (big ? cpt : tile_rows));
+  if (rb >= re) return;
+  const size_t xrow_bytes = (size_t)H * (dtype == QMOE_F32 ? 4 : 2);
+  auto x_row = [=](int rr) {
+    return (const void*)(xb + (size_t)(perm_of(pos0 + rr) / kk) * xrow_bytes);
+  };
+  auto h_out = [=](int n, int rr, const float* a) {
+    float* dst = hbuf + (size_t)(pos0 + rr) * F + n;
+    if constexpr (COH) store_coherent(dst, silu_mul(a[0], a[1]));
+    else *dst = silu_mul(a[0], a[1]);
+  };
+  auto h_row = [=](int rr) { return (const void*)(hbuf + (size_t)(pos0 + rr) * F); };
+  auto o_out = [=](int n, int rr, const float* a) {
+    float* dst = obuf + (size_t)(pos0 + rr) * H + n;
+    if constexpr (COH) store_coherent(dst, a[0]);
+    else *dst = a[0];
+  };
+#define QMOE_FFN_CASE(FM)                                                                  \
+  case FM: {                                                                               \
+    const size_t eo = (size_t)(e - t.e_begin) * layout_of(FM, N, K).total;                  \
+    if (PHASE == 0) {                                                                      \
+      const Mat mats[2] = {mat_of((const uint8_t*)t.gate + eo, FM, N, K),                  \
+                           mat_of((const uint8_t*)t.up + eo, FM, N, K)};                   \
+      if (MFMA && big && dtype == QMOE_F32)                                                \
+        mfma_cols<FM, 2, QMOE_F32>(mats, K, rb, re, m, smem, x_row, h_out);                \
+      else if (MFMA && big)                                                                \
+        mfma_cols<FM, 2, QMOE_BF16>(mats, K, rb, re, m, smem, x_row, h_out);               \
+      else valu_rows<FM, 2, RC>(mats, K, rb, re, G, m, dtype, smem, x_row, h_out);         \
+    } else {                                                                               \
+      const Mat mats[1] = {mat_of((const uint8_t*)t.down + eo, FM, N, K)};                 \
+      if (MFMA && big)                                                                     \
+        mfma_cols<FM, 1, COH ? kF32Coherent : QMOE_F32>(mats, K, rb, re, m, smem, h_row,   \
+                                                        o_out);                            \
+      else valu_rows<FM, 1, RC, COH>(mats, K, rb, re, G, m, QMOE_F32, smem, h_row, o_out); \
+    }                                                                                      \
+  } break;
+  switch (fmt) {
+    QMOE_FFN_CASE(QMOE_Q8_0)
+    QMOE_FFN_CASE(QMOE_Q4_0)
+    QMOE_FFN_CASE(QMOE_MXFP4)
+    QMOE_FFN_CASE(QMOE_Q4_K)
+    QMOE_FFN_CASE(QMOE_Q6_K)
+    default: break;
+  }
+#undef QMOE_FFN_CASE
 }
 
 // ---------------------------------------- host-side launch choices ----

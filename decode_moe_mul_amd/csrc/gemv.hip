@@ -129,13 +129,8 @@ __global__ __launch_bounds__(kBlock) void qgemv_batch_kernel(GemvBatchParams P) 
 template <int PHASE, int RC, bool MFMA>
 __global__ __launch_bounds__(kBlock, (PHASE == 1 || RC <= 2) ? 3 : 2) void ffn_decode_kernel(FfnParams P) {
   extern __shared__ __align__(16) uint8_t smem[];
-  // scalars used below, read once from the argument block
-  const int E = P.E, H = P.H, F = P.F, kk = P.k, dtype = P.x_dtype, m_max = P.m_max;
-  const int ntiles = P.ntiles, G = P.G, tile_rows = P.tile_rows;
+  const int E = P.E;
   const int32_t* perm = P.perm;
-  const char* xb = (const char*)P.x;
-  float* hbuf = P.h;
-  float* obuf = P.o;
   int* offs = (int*)smem;
   int* red = offs + E + 1;
   for (int i = threadIdx.x; i <= E; i += kBlock) offs[i] = P.offsets[i];
@@ -146,59 +141,14 @@ __global__ __launch_bounds__(kBlock, (PHASE == 1 || RC <= 2) ? 3 : 2) void ffn_d
   // the weight bases derived from them stay scalar (loads then take a
   // scalar base and a 32-bit vector offset)
   const int e = __builtin_amdgcn_readfirstlane(
-      scheduled_expert(offs, E, m_max, blockIdx.x, ntiles, P.ntiles_big, red, tile, big));
+      scheduled_expert(offs, E, P.m_max, blockIdx.x, P.ntiles, P.ntiles_big, red, tile, big));
   if (e < 0) return;
   tile = __builtin_amdgcn_readfirstlane(tile);
   big = __builtin_amdgcn_readfirstlane((int)big) != 0;
   const int pos0 = __builtin_amdgcn_readfirstlane(offs[e]);
   const int m = __builtin_amdgcn_readfirstlane(offs[e + 1]) - pos0;
-  qmoe_tier t;
-  if (!tier_of(P.tiers, P.n_tiers, e, t)) return;
-  const int fmt = PHASE == 0 ? t.fmt_gate_up : t.fmt_down;
-  const int N = PHASE == 0 ? F : H, K = PHASE == 0 ? H : F;
-  // few-row experts: weight rows [rb, re) of a row tile; many-row experts:
-  // a slice of whole matrix-core passes, N split over at most
-  // ntiles_big blocks
-  const int pass = 16 * mfma_cols_per_pass(PHASE == 0 ? 2 : 1);
-  const int cpt = ((N + P.ntiles_big - 1) / P.ntiles_big + pass - 1) / pass * pass;
-  const int rb = big ? tile * cpt : tile * tile_rows;
-  const int re = min(N, rb + (big ? cpt : tile_rows));
-  if (rb >= re) return;
-  const size_t xrow_bytes = (size_t)H * (dtype == QMOE_F32 ? 4 : 2);
-  auto x_row = [=](int rr) {
-    return (const void*)(xb + (size_t)(perm[pos0 + rr] / kk) * xrow_bytes);
-  };
-  auto h_out = [=](int n, int rr, const float* a) {
-    hbuf[(size_t)(pos0 + rr) * F + n] = silu_mul(a[0], a[1]);
-  };
-  auto h_row = [=](int rr) { return (const void*)(hbuf + (size_t)(pos0 + rr) * F); };
-  auto o_out = [=](int n, int rr, const float* a) { obuf[(size_t)(pos0 + rr) * H + n] = a[0]; };
-#define QMOE_FFN_CASE(FM)                                                                  \
-  case FM: {                                                                               \
-    const size_t eo = (size_t)(e - t.e_begin) * layout_of(FM, N, K).total;                  \
-    if (PHASE == 0) {                                                                      \
-      const Mat mats[2] = {mat_of((const uint8_t*)t.gate + eo, FM, N, K),                  \
-                           mat_of((const uint8_t*)t.up + eo, FM, N, K)};                   \
-      if (MFMA && big && dtype == QMOE_F32)                                                \
-        mfma_cols<FM, 2, QMOE_F32>(mats, K, rb, re, m, smem, x_row, h_out);                \
-      else if (MFMA && big)                                                                \
-        mfma_cols<FM, 2, QMOE_BF16>(mats, K, rb, re, m, smem, x_row, h_out);               \
-      else valu_rows<FM, 2, RC>(mats, K, rb, re, G, m, dtype, smem, x_row, h_out);         \
-    } else {                                                                               \
-      const Mat mats[1] = {mat_of((const uint8_t*)t.down + eo, FM, N, K)};                 \
-      if (MFMA && big) mfma_cols<FM, 1, QMOE_F32>(mats, K, rb, re, m, smem, h_row, o_out);         \
-      else valu_rows<FM, 1, RC>(mats, K, rb, re, G, m, QMOE_F32, smem, h_row, o_out);      \
-    }                                                                                      \
-  } break;
-  switch (fmt) {
-    QMOE_FFN_CASE(QMOE_Q8_0)
-    QMOE_FFN_CASE(QMOE_Q4_0)
-    QMOE_FFN_CASE(QMOE_MXFP4)
-    QMOE_FFN_CASE(QMOE_Q4_K)
-    QMOE_FFN_CASE(QMOE_Q6_K)
-    default: break;
-  }
-#undef QMOE_FFN_CASE
+  ffn_item<PHASE, RC, MFMA, false>(P, e, tile, big, pos0, m, smem,
+                                   [=](int i) { return perm[i]; });
 }
 
 // ------------------------------------------------------ host helpers ----

@@ -65,20 +65,6 @@ QMOE_D void stage_x_slice(const RouteParams& P, int k0, int len, float* xsl) {
   }
 }
 
-// Device-coherent scalar access for values handed between blocks of one
-// launch: agent-scope relaxed atomics, i.e. stores written through and loads
-// served past the per-XCD L2, so that no cache-wide write-back or invalidate
-// (what a device fence costs) is needed.
-QMOE_D void store_coherent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-QMOE_D float load_coherent(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// This thread's outstanding vector-memory operations have completed (its
-// written-through stores are visible device-wide) before it goes on.
-QMOE_D void drain_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
 // Sum over the wave of acc[r] for 16 rows at once: each exchange step halves
 // the rows a lane carries (xor 32, 16, 8, 4), then xor 2 and 1 finish the
 // sums.  17 lane exchanges instead of 16 separate 6-step reductions.  Lane L

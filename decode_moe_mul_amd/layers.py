@@ -117,6 +117,8 @@ class MoELayer:
                 "ffn": (qmoe.prefill_workspace(T, kt, c.E_total, c.H, c.F, dev) if prefill
                         else qmoe.ffn_workspace(T, kt, c.F, dev)),
             }
+            if not prefill and T <= 16:
+                ws["layer"] = qmoe.layer_decode_workspace(T, c.H, c.E, c.F, c.k, c.n_shared, dev)
             self._ws[key] = ws
         return self._ws[key]
 
@@ -127,16 +129,26 @@ class MoELayer:
         return (not prefill and T <= 16 and c.E <= 512
                 and ((T * kt + 63) // 64) * 64 + 16 + c.E_total <= 8192)
 
-    def forward(self, x, copy=0, prefill=False):
+    def forward(self, x, copy=0, prefill=False, one_launch=False):
         """y [T, H] for activations x [T, H] (float32 or bfloat16).  The
-        intermediate ids, p, offsets, perm, inv, o stay in the workspace dict
-        returned second."""
+        intermediate ids, p, offsets, perm, inv (and o, unless one_launch)
+        stay in the workspace dict returned second.  one_launch: the whole
+        decode layer as moe_layer_decode (T <= 16)."""
         c = self.cfg
         T = x.shape[0]
         ws = self.workspaces(T, prefill)
         L = qmoe.lib()
         s = qmoe._stream()
         kt = c.k + c.n_shared
+        if one_launch:
+            arr = self.tier_arrays[copy]
+            qmoe._check(L.moe_layer_decode(
+                arr, len(arr), c.E, c.H, c.F, qmoe._p(x), qmoe._dtype_code(x), T,
+                qmoe._p(self.Wr), qmoe._p(self.bias), c.k, c.n_shared, qmoe._p(ws["ids"]),
+                qmoe._p(ws["p"]), qmoe._p(ws["offsets"]), qmoe._p(ws["perm"]),
+                qmoe._p(ws["inv"]), qmoe._p(ws["y"]), qmoe._p(ws["layer"]), ws["layer"].numel(),
+                s), "moe_layer_decode")
+            return ws["y"], ws
         if self._fused(T, prefill):
             qmoe._check(L.moe_route_decode(
                 qmoe._p(x), qmoe._dtype_code(x), T, c.H, qmoe._p(self.Wr), qmoe._p(self.bias),

@@ -61,6 +61,9 @@ _SIGNATURES = {
     "qgemm_grouped_prefill": (_I, [ctypes.POINTER(Tier), _I, _I, _I, _I, _VP, _I, _I, _I, _VP,
                                    _VP, _VP, _VP, _SZ, _VP]),
     "moe_combine": (_I, [_VP, _VP, _VP, _I, _I, _I, _VP, _VP, _VP]),
+    "moe_layer_decode_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
+    "moe_layer_decode": (_I, [ctypes.POINTER(Tier), _I, _I, _I, _I, _VP, _I, _I, _VP, _VP, _I,
+                              _I, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "qmoe_profile_enable": (_I, [_I]),
     "qmoe_profile_reset": (_I, []),
     "qmoe_profile_only": (_I, [ctypes.c_char_p]),
@@ -344,6 +347,38 @@ def combine(o, inv_perm, p, T, k, H, shared=None, out=None):
     _check(lib().moe_combine(_p(o), _p(inv_perm), _p(p), T, k, H, _p(shared), _p(out),
                              _stream()), "moe_combine")
     return out
+
+
+def layer_decode_workspace(T, H, E, F, k, n_shared=0, device="cuda"):
+    """Workspace of moe_layer_decode: zero-filled, as its barrier counter requires."""
+    torch = _torch()
+    n = lib().moe_layer_decode_workspace_size(T, H, E, F, k, n_shared)
+    return torch.zeros(max(int(n), 1), dtype=torch.uint8, device=device)
+
+
+def layer_decode(tiers, E, H, F, x, Wr, bias, k, n_shared=0, out=None, ws=None):
+    """The whole routed-expert layer for decode rows (T <= 16) in one launch:
+    y [T, H] and the routing ids, p, offsets, perm, inv_perm."""
+    torch = _torch()
+    _cuda_contig(x, Wr, bias)
+    T = x.shape[0]
+    dev = x.device
+    kt, E_total = k + n_shared, E + n_shared
+    arr = tiers if isinstance(tiers, ctypes.Array) else tiers_struct(tiers)
+    ids = torch.empty((T, kt), dtype=torch.int32, device=dev)
+    p = torch.empty((T, kt), dtype=torch.float32, device=dev)
+    offsets = torch.empty(E_total + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(max(T * kt, 1), dtype=torch.int32, device=dev)
+    inv = torch.empty(max(T * kt, 1), dtype=torch.int32, device=dev)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = layer_decode_workspace(T, H, E, F, k, n_shared, dev)
+    _check(lib().moe_layer_decode(arr, len(arr), E, H, F, _p(x), _dtype_code(x), T, _p(Wr),
+                                  _p(bias), k, n_shared, _p(ids), _p(p), _p(offsets), _p(perm),
+                                  _p(inv), _p(out), _p(ws), ws.numel(), _stream()),
+           "moe_layer_decode")
+    return out, ids, p, offsets, perm, inv
 
 
 # -------------------------------------------------------------- profiling --

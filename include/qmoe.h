@@ -298,6 +298,42 @@ int qgemm_grouped_prefill(const qmoe_tier *tiers, int n_tiers, int E, int H,
 int moe_combine(const float *o, const int32_t *inv_perm, const float *p, int T,
                 int k, int H, const float *shared, float *y, void *stream);
 
+/* moe_layer_decode: the whole routed-expert layer of a decode step in one
+ * launch ([P2] "瓶颈分析": router top-k over the experts, the selected
+ * experts' SwiGLU FFNs, their weighted sum; "优化策略二/三": tiers of mixed
+ * precision in one layer).  Computes what
+ *   moe_route_decode(x, Wr, bias, E, k, n_shared) -> ids, p, offsets, perm,
+ *   inv_perm;  moe_ffn_tiered(tiers, E + n_shared, H, F, x, T, k + n_shared)
+ *   -> o;  moe_combine(o, inv_perm, p, T, k + n_shared, H, NULL) -> y
+ * computes, with the same arithmetic: the outputs are equal bit for bit
+ * whenever both paths pick the same dot-product blocking (always, unless
+ * staged rows of length H or F need more than about 60 KB of LDS).  A
+ * cooperative grid of co-resident blocks runs the phases separated by three
+ * device-wide barriers (a counter in the workspace).
+ * Arguments: tiers cover ids [0, E + n_shared) (shared experts are ids E..,
+ * always selected with weight 1); x [T, H] (x_dtype), Wr [E, H] fp32, bias [E]
+ * fp32 or NULL; outputs ids/p [T, k+n_shared], offsets [E+n_shared+1], perm
+ * and inv_perm [T*(k+n_shared)], y [T, H] fp32.  x, Wr and y 16-byte aligned.
+ * Limits: T <= 16, 1 <= k <= min(E, 64), E <= 512, H % 4 == 0, plus
+ * moe_ffn_tiered's (UNSUPPORTED when the routing of T*(k+n_shared) rows and
+ * the staged rows do not fit 64 KB of LDS, or the device cannot hold the
+ * grid).  T == 0 writes zero offsets and nothing else.
+ * Workspace: moe_layer_decode_workspace_size(T, H, E, F, k, n_shared) bytes,
+ * 256-byte aligned, whose first 12288 bytes (the barrier counters) must be
+ * zero before the first call that uses it; every call leaves them zero again.
+ * A nonzero first word (uint32 at byte 0) after a call means a barrier wait
+ * ran out (about a second) and the outputs are invalid; the workspace must
+ * then be zeroed again.  Calls sharing one workspace must not run
+ * concurrently. */
+size_t moe_layer_decode_workspace_size(int T, int H, int E, int F, int k,
+                                       int n_shared);
+int moe_layer_decode(const qmoe_tier *tiers, int n_tiers, int E, int H, int F,
+                     const void *x, int x_dtype, int T, const float *Wr,
+                     const float *bias, int k, int n_shared, int32_t *ids,
+                     float *p, int32_t *offsets, int32_t *perm,
+                     int32_t *inv_perm, float *y, void *ws, size_t ws_bytes,
+                     void *stream);
+
 /* ----------------------------------------------------------- profiling --
  * Optional per-kernel timing with HIP events recorded around every launch the
  * library makes while enabled (on the launch stream).  qmoe_profile_read

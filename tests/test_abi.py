@@ -173,3 +173,23 @@ def test_t5_ternary_entry_points_and_limits(L):
     assert b"matrix 1" in L.qmoe_last_error()
     descs[1] = qmoe.GemvDesc(3, 8, 256, 0, 1, 0, 256000, 256000, 256000)
     assert L.qgemv_batch(descs, 2, None) == -2
+
+
+def test_one_launch_layer_validation(L):
+    from decode_moe_mul_amd import qmoe
+    fake = ctypes.c_void_p(256 * 1000)  # never dereferenced: every call below fails validation
+    arr = (qmoe.Tier * 1)(qmoe.Tier(0, 16, 0, 0, 256000, 256000, 256000))
+    need = L.moe_layer_decode_workspace_size(4, 64, 16, 64, 2, 0)
+    # counter block + split-K partials + h [A, F] + o [A, H], each 256-aligned
+    assert need == 12288 + 256 + 2048 + 2048
+    args = lambda T, E, k, ns, ws: (arr, 1, E, 64, 64, fake, 0, T, fake, None, k, ns, fake, fake,
+                                    fake, fake, fake, fake, fake, ws, None)
+    assert L.moe_layer_decode(*args(17, 16, 2, 0, 1 << 30)) == -2      # rows beyond 16
+    assert L.moe_layer_decode(*args(4, 16, 0, 0, 1 << 30)) == -1       # k = 0
+    assert L.moe_layer_decode(*args(4, 16, 17, 0, 1 << 30)) == -1      # k > E
+    assert L.moe_layer_decode(*args(4, 600, 8, 0, 1 << 30)) == -2      # E > 512
+    assert L.moe_layer_decode(*args(4, 16, 2, 0, need - 1)) == -3      # workspace
+    # tiers must cover the shared experts too
+    assert L.moe_layer_decode(*args(4, 16, 2, 1, 1 << 30)) == -1
+    assert b"cover" in L.qmoe_last_error()
+    assert L.moe_layer_decode_workspace_size(-1, 64, 16, 64, 2, 0) == 0

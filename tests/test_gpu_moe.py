@@ -44,10 +44,10 @@ def _x(cfg, T, seed=0):
     return x, to_gpu(x)
 
 
-def _check_layer(cfg, T, rows_checked=None, seed=0, prefill=False, cols=None):
+def _check_layer(cfg, T, rows_checked=None, seed=0, prefill=False, cols=None, one_launch=False):
     layer = _layer(cfg)
     x, xg = _x(cfg, T, seed)
-    y, ws = layer.forward(xg, prefill=prefill)
+    y, ws = layer.forward(xg, prefill=prefill, one_launch=one_launch)
     y = to_np(y)
     ids = to_np(ws["ids"])
     p = to_np(ws["p"])
@@ -243,3 +243,75 @@ def test_prefill_chunk_full_size_sampled():
     the oracle checks 35 sampled tokens on all 2048 outputs."""
     rows = np.concatenate([np.arange(0, 2048, 64), [1, 2046, 2047]])
     _check_layer(configs.PREFILL, 2048, rows_checked=rows, prefill=True)
+
+
+# ------------------------------------------------ one-launch decode layer --
+
+ONE_LAUNCH_CASES = [(configs.TINY, 4), (SMALL_TIERED, 1), (SMALL_TIERED, 5), (SMALL_TIERED, 16),
+                    (SMALL_SHARED, 16), (SMALL_SHARED, 2), (configs.TIERED, 1),
+                    (configs.TIERED, 6), (configs.TIERED, 3)]
+
+
+def _counter_words(ws):
+    """The barrier counters (first 12288 bytes of the workspace): nonzero
+    words, at most 3 listed; [] when all are zero as every call must leave them."""
+    w = to_np(ws["layer"][:12288].view(torch.int32))
+    return w[w != 0][:3].tolist()
+
+
+@pytest.mark.parametrize("cfg,T", ONE_LAUNCH_CASES, ids=lambda v: getattr(v, "name", v))
+def test_one_launch_layer_matches_oracle(cfg, T):
+    _, _, ws = _check_layer(cfg, T, seed=7, one_launch=True)
+    assert _counter_words(ws) == []
+
+
+@pytest.mark.parametrize("cfg,T", ONE_LAUNCH_CASES, ids=lambda v: getattr(v, "name", v))
+def test_one_launch_layer_equals_separate_calls_bitexactly(cfg, T):
+    """Same arithmetic as route_decode + ffn_tiered + combine: ids, p,
+    offsets, perm, inv_perm and y are equal bit for bit."""
+    layer = _layer(cfg)
+    _, xg = _x(cfg, T, seed=8)
+    y, ws = layer.forward(xg)
+    ref = {k: to_np(ws[k]).copy() for k in ("y", "ids", "p", "offsets", "perm", "inv")}
+    for k in ("y", "ids", "p", "offsets", "perm", "inv"):
+        ws[k].fill_(-7)
+    layer.forward(xg, one_launch=True)
+    for k, v in ref.items():
+        got = to_np(ws[k])
+        if v.dtype == np.float32:
+            assert_bitexact(got, v, f"{cfg.name} T={T} {k}")
+        else:
+            assert (got == v).all(), f"{cfg.name} T={T} {k}"
+    assert _counter_words(ws) == []
+
+
+def test_one_launch_grouped_full_size_sampled():
+    """The 16-row grouped layer in one launch (hidden 7168: the dot-product
+    blocking drops to 2 rows, so the shared expert runs on the matrix cores
+    in both phases)."""
+    cols = np.sort(np.random.default_rng(1).choice(7168, 64, replace=False))
+    _check_layer(configs.GROUPED, 16, rows_checked=[2, 11], cols=cols, one_launch=True)
+
+
+def test_one_launch_repeated_calls_reuse_the_counter():
+    """Calls of different row counts back to back on one workspace each leave
+    the barrier counter at zero and give the same results as before."""
+    cfg = configs.TIERED
+    layer = _layer(cfg)
+    outs = {}
+    for rep in range(2):
+        for T in (1, 6, 1, 16):
+            _, xg = _x(cfg, T, seed=10 + T)
+            y, ws = layer.forward(xg, one_launch=True)
+            yv = to_np(y).copy()
+            assert _counter_words(ws) == []
+            if T in outs:
+                assert (outs[T] == yv).all()
+            outs[T] = yv
+
+
+def test_one_launch_limits():
+    layer = _layer(WIDE_HIDDEN)
+    _, xg = _x(WIDE_HIDDEN, 1)
+    with pytest.raises(RuntimeError, match="do not fit LDS"):
+        layer.forward(xg, one_launch=True)
