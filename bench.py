@@ -135,8 +135,8 @@ def cpu_baseline(budget_s=20.0):
 # kernel sources and ignored once they change.
 CAL_BYTES = 256 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ffn_gate_up_traffic.json")
-KERNEL_SOURCES = ("decode_moe_mul_amd/csrc/gemv.hip", "decode_moe_mul_amd/csrc/common.hpp",
-                  "decode_moe_mul_amd/csrc/dequant.hpp")
+KERNEL_SOURCES = ("decode_moe_mul_amd/csrc/gemv.hip", "decode_moe_mul_amd/csrc/decode.hpp",
+                  "decode_moe_mul_amd/csrc/common.hpp", "decode_moe_mul_amd/csrc/dequant.hpp")
 
 
 def kernel_hash():
