@@ -13,6 +13,8 @@ path computes, in float64 NumPy:
 * ``oracle.moe``      -- dense quantized GEMV, router + softmax top-k,
   expert permutation, expert FFN with SwiGLU, weighted combine, the whole
   routed-expert layer, and the per-element error bounds used for parity.
+* ``oracle.mx``       -- MXFP8 (E4M3) activation quantization and the MX GEMM
+  reference for MXFP4 weights on block-scaled matrix cores.
 * ``oracle.brute``    -- pure-Python scalar loops for tiny cases, used only to
   cross-check the vectorised oracle.
 
