@@ -291,6 +291,44 @@ def ternary_gemv(torch, steps):
     return res
 
 
+def mx_gemm(torch, calls=20):
+    """MXFP4 weights x MXFP8 activations on the block-scaled matrix cores
+    (qgemm_mxfp4_mxfp8) for 2048 activation rows: the tail tier's expert
+    shapes (gate/up [640, 2048], down [2048, 640]) and a Llama-3-8B MLP shape
+    ([14336, 4096]).  Reported beside it: the activation quantizer, and
+    dequantize-to-fp16 + torch.matmul (the library GEMM) on the same matrix
+    as context."""
+    from decode_moe_mul_amd import qmoe, synth
+    R = 2048
+    out = {"rows": R, "peak_tflops": 5000.0, "peak_note": "dense fp8 MFMA", "shapes": {}}
+    for name, N, K in (("tail_gate_up", 640, 2048), ("tail_down", 2048, 640),
+                       ("llama_up", 14336, 4096)):
+        W = synth.normal_device((N, K), 0.02, 5, synth.UP, 0, "cuda")
+        buf = qmoe.quantize("mxfp4", W)
+        x = torch.from_numpy(synth.normal((R, K), 1.0, 6, synth.ACT, 0)).cuda()
+        codes, scales = qmoe.quantize_act_mxfp8(x)
+        y = torch.empty((R, N), dtype=torch.float32, device="cuda")
+        qmoe.gemm_mxfp4_mxfp8(buf, N, K, codes, scales, out=y)
+        ms = _events_ms(torch, lambda i: qmoe.gemm_mxfp4_mxfp8(buf, N, K, codes, scales, out=y),
+                        calls)
+        qms = _events_ms(torch, lambda i: qmoe.quantize_act_mxfp8(x), calls)
+        w16 = qmoe.dequantize("mxfp4", buf, N, K).half()
+        x16 = x.half()
+        torch.matmul(x16, w16.t())
+        dms = _events_ms(torch, lambda i: torch.matmul(x16, w16.t()), calls)
+        flops = 2.0 * R * N * K
+        out["shapes"][name] = {
+            "N": N, "K": K, "us": round(ms * 1e3, 2),
+            "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+            "frac": round(flops / (ms * 1e-3) / 5.0e15, 4),
+            "quantize_us": round(qms * 1e3, 2),
+            "fp16_library_gemm_us": round(dms * 1e3, 2)}
+        del W, buf, w16
+    torch.cuda.empty_cache()
+    log(f"mx gemm: {out['shapes']}")
+    return out
+
+
 def prefill_chunk(torch, calls=10):
     """The tiered 512-expert layer on a 2048-row prefill chunk: router GEMM,
     top-k, permutation, grouped gate/up and down on the matrix cores, combine.
@@ -441,6 +479,7 @@ def main():
     dense = None if a.decode_only else dense_gemv(torch, a.steps)
     ternary = None if a.decode_only else ternary_gemv(torch, a.steps)
     prefill = None if a.decode_only else prefill_chunk(torch)
+    mx = None if a.decode_only else mx_gemm(torch)
 
     t = stored_traffic()
     traffic = None if t is None else int(t["traffic_bytes_per_launch"])
@@ -486,6 +525,8 @@ def main():
     out["one_launch_layer"] = one_launch
     if prefill is not None:
         out["prefill"] = prefill
+    if mx is not None:
+        out["mx_gemm"] = mx
     if not a.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         out["cpu_baseline"] = cpu_baseline()

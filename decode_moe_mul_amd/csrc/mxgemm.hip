@@ -1,0 +1,249 @@
+// MXFP4 weights x MXFP8 activations on the gfx950 block-scaled matrix cores.
+//
+// The "RTX 4080 SUPER native Windows 27B: NInfer 80 SM port" page (its list of
+// hardware limits) names 4-bit weight and activation matrix ops as a tensor
+// core feature its GPU lacks, so its 4-bit tier dequantizes on chip.  CDNA4
+// multiplies block-scaled FP8/FP6/FP4 operands directly, one E8M0 scale per
+// 32 values along K (OCP Microscaling Formats v1.0), with the two operands in
+// different element types.  Here the MXFP4 weights are used as stored (codes
+// and scales straight from HBM, no dequantization) and the activations are
+// quantized once to MXFP8 with E4M3 elements:
+//  * qquantize_act_mxfp8: per 32 values along K, E = floor(log2 max|x|) - 8,
+//    stored as E + 127 clamped to [0, 254] (0 for an all-zero block); each
+//    element is |x| / 2^E rounded to the nearest E4M3 value, ties to even,
+//    saturating at 448, with the sign of x;
+//  * qgemm_mxfp4_mxfp8: y[r, n] = sum_k w[n, k] x_q[r, k], one
+//    v_mfma_scale_f32_16x16x128_f8f6f4 per 16 x 16 output tile and 128 values
+//    of K (fp32 accumulation).
+//
+// Operand layout of that instruction (measured on the device with a one-wave
+// probe against a CPU model): lane l = 16 g + i supplies
+//  * B (FP4, 4 registers): column i, K values 32 g .. 32 g + 31 in nibble
+//    order (low nibble first): exactly unit g of the step in weight row i, so
+//    a lane loads one 16-byte unit of codes;
+//  * A (FP8, 8 registers): row i, K values 16 g .. 16 g + 15 (bytes 0..15)
+//    and 64 + 16 g .. 64 + 16 g + 15 (bytes 16..31);
+//  * scale bytes (byte 0 of a register): the scale of K block g (values
+//    32 g .. 32 g + 31) of its row (A) or column (B), whichever lanes hold
+//    that block's data;
+//  * result: rows 4 g .. 4 g + 3 of column i.
+#include "common.hpp"
+
+#pragma clang fp contract(off)
+
+namespace qmoe {
+
+typedef int mx_v8i __attribute__((ext_vector_type(8)));
+typedef float mx_v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kMxWaves = 4;
+constexpr int kMxBlock = 64 * kMxWaves;
+constexpr int kMxMI = 4;  // 16-row groups per tile: 64 rows
+constexpr int kMxNB = 2;  // 16-column blocks per wave: 4 x 2 x 16 = 128 columns
+constexpr int kMxBM = 16 * kMxMI, kMxBN = 16 * kMxNB * kMxWaves;
+
+// ------------------------------------------------ activation quantizer ----
+// |x| / 2^E (in [0, 512)) to the nearest E4M3 magnitude code, ties to even,
+// saturating at 448 (code 0x7E).  Exact: the subnormal range is an integer
+// multiple of 2^-9, the normal range keeps 3 of the 23 mantissa bits.
+QMOE_D uint32_t e4m3_code_of(float m) {
+  if (!(m < 448.f)) return 0x7Eu;
+  if (m < 0.015625f) return (uint32_t)__builtin_rintf(m * 512.f);  // 2^-6: subnormals
+  const uint32_t b = __builtin_bit_cast(uint32_t, m);
+  const uint32_t r = b + 0x7FFFFu + ((b >> 20) & 1u);  // round 23 -> 3 mantissa bits
+  const uint32_t code = ((((r >> 23) & 0xFFu) - 120u) << 3) | ((r >> 20) & 7u);
+  return code > 0x7Eu ? 0x7Eu : code;
+}
+
+__global__ __launch_bounds__(256) void quantize_act_mxfp8_kernel(const void* x, int x_dtype,
+                                                                 int R, int K, uint8_t* codes,
+                                                                 uint8_t* scales) {
+  const int nbk = K >> 5;
+  const long long blk = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (blk >= (long long)R * nbk) return;
+  const long long at = blk * 32;
+  float v[32];
+  if (x_dtype == QMOE_F32) {
+    const float4* p = (const float4*)((const float*)x + at);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float4 f = p[i];
+      v[4 * i] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
+    }
+  } else {
+    const uint4* p = (const uint4*)((const uint16_t*)x + at);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 q = p[i];
+      const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[8 * i + 2 * j] = bf16_bits_to_f32(w[j] & 0xFFFFu);
+        v[8 * i + 2 * j + 1] = bf16_bits_to_f32(w[j] >> 16);
+      }
+    }
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  int e = 0;  // E8M0 byte
+  if (amax > 0.f) {
+    int ex;
+    frexpf(amax, &ex);  // amax = f * 2^ex, f in [0.5, 1)
+    e = min(max(127 + (ex - 1) - 8, 0), 254);
+  }
+  scales[blk] = (uint8_t)e;
+  uint32_t out[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float xv = v[4 * i + j];
+      uint32_t c = e4m3_code_of(ldexpf(fabsf(xv), 127 - e));
+      if (xv < 0.f) c |= 0x80u;
+      word |= c << (8 * j);
+    }
+    out[i] = word;
+  }
+  uint4* dst = (uint4*)(codes + at);
+  dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
+  dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
+}
+
+// ----------------------------------------------------------- the GEMM ----
+struct MxParams {
+  const uint8_t* wq;  // codes plane [N][K/2]
+  const uint8_t* ws;  // E8M0 plane [N][K/32]
+  const uint8_t* xq;  // [R][K] E4M3
+  const uint8_t* xs;  // [R][K/32] E8M0
+  float* y;           // [R][N]
+  int N, K, R;
+};
+
+struct MxA {  // one lane's A operand of one 16-row group and step
+  uint4 lo, hi;
+  uint32_t s;
+};
+struct MxB {  // one lane's B operand of one 16-column block and step
+  uint4 q;
+  uint32_t s;
+};
+
+// Block (bx, by): rows by * 64 .., columns bx * 128 ..; wave w takes columns
+// w * 32 .. w * 32 + 31 (two 16-column blocks) of every row group.  Loads of
+// step s + 1 are in flight while step s is multiplied.  Rows and columns past
+// the ends re-read the last one (never stored), so every load is
+// unconditional.
+__global__ __launch_bounds__(kMxBlock) void mxfp4_gemm_kernel(MxParams P) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int li = lane & 15, g = lane >> 4;
+  const int K = P.K, nbk = K >> 5, nsteps = K >> 7;
+  const int r0 = blockIdx.y * kMxBM, c0 = blockIdx.x * kMxBN + wave * (16 * kMxNB);
+  uint32_t arow[kMxMI], bcol[kMxNB];
+#pragma unroll
+  for (int i = 0; i < kMxMI; ++i) arow[i] = (uint32_t)min(r0 + 16 * i + li, P.R - 1);
+#pragma unroll
+  for (int b = 0; b < kMxNB; ++b) bcol[b] = (uint32_t)min(c0 + 16 * b + li, P.N - 1);
+  auto load = [&](int s, MxA (&a)[kMxMI], MxB (&w)[kMxNB]) {
+    const uint32_t k0 = (uint32_t)s * 128u, blk = (uint32_t)s * 4u + (uint32_t)g;
+#pragma unroll
+    for (int i = 0; i < kMxMI; ++i) {
+      const uint8_t* row = P.xq + arow[i] * (uint32_t)K + k0;
+      a[i].lo = *(const uint4*)(row + 16u * g);
+      a[i].hi = *(const uint4*)(row + 64u + 16u * g);
+      a[i].s = P.xs[arow[i] * (uint32_t)nbk + blk];
+    }
+#pragma unroll
+    for (int b = 0; b < kMxNB; ++b) {
+      w[b].q = *(const uint4*)(P.wq + bcol[b] * (uint32_t)(K >> 1) + 16u * blk);
+      w[b].s = P.ws[bcol[b] * (uint32_t)nbk + blk];
+    }
+  };
+  mx_v4f acc[kMxMI][kMxNB];
+#pragma unroll
+  for (int i = 0; i < kMxMI; ++i)
+#pragma unroll
+    for (int b = 0; b < kMxNB; ++b) acc[i][b] = mx_v4f{0.f, 0.f, 0.f, 0.f};
+  auto mma = [&](const MxA (&a)[kMxMI], const MxB (&w)[kMxNB]) {
+#pragma unroll
+    for (int i = 0; i < kMxMI; ++i) {
+      const mx_v8i av = {(int)a[i].lo.x, (int)a[i].lo.y, (int)a[i].lo.z, (int)a[i].lo.w,
+                         (int)a[i].hi.x, (int)a[i].hi.y, (int)a[i].hi.z, (int)a[i].hi.w};
+#pragma unroll
+      for (int b = 0; b < kMxNB; ++b) {
+        const mx_v8i bv = {(int)w[b].q.x, (int)w[b].q.y, (int)w[b].q.z, (int)w[b].q.w, 0, 0, 0, 0};
+        acc[i][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            av, bv, acc[i][b], 0 /* A: FP8 E4M3 */, 4 /* B: FP4 E2M1 */, 0, (int)a[i].s, 0,
+            (int)w[b].s);
+      }
+    }
+  };
+  MxA a0[kMxMI], a1[kMxMI];
+  MxB w0[kMxNB], w1[kMxNB];
+  const int last = nsteps - 1;
+  load(0, a0, w0);
+  int s = 0;
+  for (; s + 1 < nsteps; s += 2) {
+    load(s + 1, a1, w1);
+    mma(a0, w0);
+    load(min(s + 2, last), a0, w0);
+    mma(a1, w1);
+  }
+  if (s < nsteps) mma(a0, w0);
+  // lane holds rows 4 g + j of each row group, column li of each block
+#pragma unroll
+  for (int i = 0; i < kMxMI; ++i)
+#pragma unroll
+    for (int b = 0; b < kMxNB; ++b) {
+      const int col = c0 + 16 * b + li;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = r0 + 16 * i + 4 * g + j;
+        if (row < P.R && col < P.N) P.y[(size_t)row * P.N + col] = acc[i][b][j];
+      }
+    }
+}
+
+}  // namespace qmoe
+
+using namespace qmoe;
+
+extern "C" {
+
+int qquantize_act_mxfp8(const void* x, int x_dtype, int R, int K, uint8_t* codes,
+                        uint8_t* scales, void* stream) {
+  if (R < 0 || K <= 0 || K % 32)
+    return fail(QMOE_ERR_INVALID_ARG, "qquantize_act_mxfp8: R=%d K=%d (K %% 32 != 0)", R, K);
+  if (x_dtype != QMOE_F32 && x_dtype != QMOE_BF16)
+    return fail(QMOE_ERR_UNSUPPORTED, "qquantize_act_mxfp8: unknown x_dtype %d", x_dtype);
+  if (R == 0) return QMOE_OK;
+  if (!x || !codes || !scales) return fail(QMOE_ERR_INVALID_ARG, "qquantize_act_mxfp8: null pointer");
+  if (!QMOE_ALIGNED(x, 16) || !QMOE_ALIGNED(codes, 16))
+    return fail(QMOE_ERR_INVALID_ARG, "qquantize_act_mxfp8: misaligned x/codes");
+  const long long blocks = (long long)R * (K / 32);
+  const dim3 grid((unsigned)((blocks + 255) / 256));
+  return QMOE_LAUNCH("quantize_act_mxfp8", quantize_act_mxfp8_kernel, grid, 256, 0,
+                     (hipStream_t)stream, x, x_dtype, R, K, codes, scales);
+}
+
+int qgemm_mxfp4_mxfp8(const void* W, int N, int K, const uint8_t* codes, const uint8_t* scales,
+                      int R, float* y, void* stream) {
+  if (N < 0 || R < 0 || K <= 0 || K % 128)
+    return fail(QMOE_ERR_INVALID_ARG, "qgemm_mxfp4_mxfp8: N=%d R=%d K=%d (K %% 128 != 0)", N,
+                R, K);
+  if ((long long)N * K >= (1LL << 32) || (long long)R * K >= (1LL << 32))
+    return fail(QMOE_ERR_UNSUPPORTED, "qgemm_mxfp4_mxfp8: offsets beyond 32 bits");
+  if (N == 0 || R == 0) return QMOE_OK;
+  if (!W || !codes || !scales || !y)
+    return fail(QMOE_ERR_INVALID_ARG, "qgemm_mxfp4_mxfp8: null pointer");
+  if (!QMOE_ALIGNED(W, 256) || !QMOE_ALIGNED(codes, 16))
+    return fail(QMOE_ERR_INVALID_ARG, "qgemm_mxfp4_mxfp8: misaligned W/codes");
+  const Layout L = layout_of(QMOE_MXFP4, N, K);
+  MxParams P{(const uint8_t*)W + L.off[0], (const uint8_t*)W + L.off[1], codes, scales, y, N, K, R};
+  const dim3 grid((unsigned)((N + kMxBN - 1) / kMxBN), (unsigned)((R + kMxBM - 1) / kMxBM));
+  if (grid.y > 65535) return fail(QMOE_ERR_UNSUPPORTED, "qgemm_mxfp4_mxfp8: R=%d too large", R);
+  return QMOE_LAUNCH("mxfp4_gemm", mxfp4_gemm_kernel, grid, kMxBlock, 0, (hipStream_t)stream, P);
+}
+
+}  // extern "C"

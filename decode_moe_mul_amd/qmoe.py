@@ -61,6 +61,8 @@ _SIGNATURES = {
     "qgemm_grouped_prefill": (_I, [ctypes.POINTER(Tier), _I, _I, _I, _I, _VP, _I, _I, _I, _VP,
                                    _VP, _VP, _VP, _SZ, _VP]),
     "moe_combine": (_I, [_VP, _VP, _VP, _I, _I, _I, _VP, _VP, _VP]),
+    "qquantize_act_mxfp8": (_I, [_VP, _I, _I, _I, _VP, _VP, _VP]),
+    "qgemm_mxfp4_mxfp8": (_I, [_VP, _I, _I, _VP, _VP, _I, _VP, _VP]),
     "moe_layer_decode_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "moe_layer_decode": (_I, [ctypes.POINTER(Tier), _I, _I, _I, _I, _VP, _I, _I, _VP, _VP, _I,
                               _I, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
@@ -346,6 +348,31 @@ def combine(o, inv_perm, p, T, k, H, shared=None, out=None):
         out = torch.empty((T, H), dtype=torch.float32, device=o.device)
     _check(lib().moe_combine(_p(o), _p(inv_perm), _p(p), T, k, H, _p(shared), _p(out),
                              _stream()), "moe_combine")
+    return out
+
+
+def quantize_act_mxfp8(x):
+    """Activations [R, K] (float32 or bfloat16) -> MXFP8 codes [R, K] uint8
+    (E4M3) and scales [R, K/32] uint8 (E8M0)."""
+    torch = _torch()
+    _cuda_contig(x)
+    R, K = x.shape
+    codes = torch.empty((R, K), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((R, max(K // 32, 1)), dtype=torch.uint8, device=x.device)
+    _check(lib().qquantize_act_mxfp8(_p(x), _dtype_code(x), R, K, _p(codes), _p(scales),
+                                     _stream()), "qquantize_act_mxfp8")
+    return codes, scales
+
+
+def gemm_mxfp4_mxfp8(W, N, K, codes, scales, out=None):
+    """y [R, N] = W (MXFP4 [N, K]) times the MXFP8 activations."""
+    torch = _torch()
+    _cuda_contig(W, codes, scales)
+    R = codes.shape[0]
+    if out is None:
+        out = torch.empty((R, N), dtype=torch.float32, device=codes.device)
+    _check(lib().qgemm_mxfp4_mxfp8(_p(W), N, K, _p(codes), _p(scales), R, _p(out), _stream()),
+           "qgemm_mxfp4_mxfp8")
     return out
 
 

@@ -298,6 +298,26 @@ int qgemm_grouped_prefill(const qmoe_tier *tiers, int n_tiers, int E, int H,
 int moe_combine(const float *o, const int32_t *inv_perm, const float *p, int T,
                 int k, int H, const float *shared, float *y, void *stream);
 
+/* ---------------------------------------------- block-scaled MX GEMM ----
+ * MXFP4 weights multiplied on the gfx950 block-scaled matrix cores, without
+ * dequantization ([P1] "NInfer 80 SM port", list of hardware limits: 4-bit
+ * weight x low-precision activation matrix ops are what its GPU lacks).  The
+ * activations are quantized once to MXFP8 (OCP Microscaling v1.0, E4M3
+ * elements, one E8M0 scale per 32 values along K):
+ *   E = floor(log2 max|x|) - 8 per block, stored as E + 127 clamped to
+ *   [0, 254] (0 for an all-zero block); code = nearest E4M3 value to
+ *   |x| / 2^E, ties to even, saturating at 448, sign of x.
+ * qquantize_act_mxfp8: x [R, K] (x_dtype) -> codes [R, K] (E4M3 bytes) and
+ * scales [R, K/32] (E8M0 bytes).  K % 32 == 0; x and codes 16-byte aligned.
+ * qgemm_mxfp4_mxfp8: y [R, N] fp32 = sum_k w[n, k] * xq[r, k] for MXFP4
+ * weights W [N, K] (qmoe layout, 256-byte aligned) and MXFP8 activations as
+ * qquantize_act_mxfp8 writes them; every product is exact, sums are fp32 in
+ * the matrix cores.  K % 128 == 0; N*K and R*K < 2^32.                     */
+int qquantize_act_mxfp8(const void *x, int x_dtype, int R, int K,
+                        uint8_t *codes, uint8_t *scales, void *stream);
+int qgemm_mxfp4_mxfp8(const void *W, int N, int K, const uint8_t *codes,
+                      const uint8_t *scales, int R, float *y, void *stream);
+
 /* moe_layer_decode: the whole routed-expert layer of a decode step in one
  * launch ([P2] "瓶颈分析": router top-k over the experts, the selected
  * experts' SwiGLU FFNs, their weighted sum; "优化策略二/三": tiers of mixed

@@ -193,3 +193,15 @@ def test_one_launch_layer_validation(L):
     assert L.moe_layer_decode(*args(4, 16, 2, 1, 1 << 30)) == -1
     assert b"cover" in L.qmoe_last_error()
     assert L.moe_layer_decode_workspace_size(-1, 64, 16, 64, 2, 0) == 0
+
+
+def test_mx_gemm_validation(L):
+    fake = ctypes.c_void_p(256 * 1000)  # never dereferenced: every call below fails validation
+    assert L.qquantize_act_mxfp8(fake, 0, 4, 48, fake, fake, None) == -1     # K % 32
+    assert L.qquantize_act_mxfp8(fake, 5, 4, 64, fake, fake, None) == -2     # dtype
+    assert L.qquantize_act_mxfp8(None, 0, 4, 64, fake, fake, None) == -1     # null
+    assert L.qquantize_act_mxfp8(fake, 0, 0, 64, fake, fake, None) == 0      # no rows
+    assert L.qgemm_mxfp4_mxfp8(fake, 16, 96, fake, fake, 4, fake, None) == -1  # K % 128
+    assert L.qgemm_mxfp4_mxfp8(ctypes.c_void_p(256 * 1000 + 16), 16, 128, fake, fake, 4, fake,
+                               None) == -1                                    # W alignment
+    assert L.qgemm_mxfp4_mxfp8(fake, 0, 128, fake, fake, 4, fake, None) == 0
