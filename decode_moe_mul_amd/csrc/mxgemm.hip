@@ -38,9 +38,10 @@ typedef float mx_v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kMxWaves = 4;
 constexpr int kMxBlock = 64 * kMxWaves;
-constexpr int kMxMI = 4;  // 16-row groups per tile: 64 rows
-constexpr int kMxNB = 2;  // 16-column blocks per wave: 4 x 2 x 16 = 128 columns
-constexpr int kMxBM = 16 * kMxMI, kMxBN = 16 * kMxNB * kMxWaves;
+constexpr int kMxMI = 4;  // 16-row groups per wave: 64 rows
+constexpr int kMxNB = 4;  // 16-column blocks per wave: 64 columns
+// the 4 waves as 2 x 2: a block computes 128 rows x 128 columns
+constexpr int kMxBM = 2 * 16 * kMxMI, kMxBN = 2 * 16 * kMxNB;
 
 // ------------------------------------------------ activation quantizer ----
 // |x| / 2^E (in [0, 512)) to the nearest E4M3 magnitude code, ties to even,
@@ -130,16 +131,17 @@ struct MxB {  // one lane's B operand of one 16-column block and step
   uint32_t s;
 };
 
-// Block (bx, by): rows by * 64 .., columns bx * 128 ..; wave w takes columns
-// w * 32 .. w * 32 + 31 (two 16-column blocks) of every row group.  Loads of
-// step s + 1 are in flight while step s is multiplied.  Rows and columns past
-// the ends re-read the last one (never stored), so every load is
-// unconditional.
+// Block (bx, by): rows by * 128 .., columns bx * 128 ..; wave w takes the
+// 64 x 64 quarter (w >> 1, w & 1): 4 row groups x 4 column blocks, 16 matrix
+// ops per step against 4 + 4 operand loads.  Loads of step s + 1 are in
+// flight while step s is multiplied.  Rows and columns past the ends re-read
+// the last one (never stored), so every load is unconditional.
 __global__ __launch_bounds__(kMxBlock) void mxfp4_gemm_kernel(MxParams P) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int li = lane & 15, g = lane >> 4;
   const int K = P.K, nbk = K >> 5, nsteps = K >> 7;
-  const int r0 = blockIdx.y * kMxBM, c0 = blockIdx.x * kMxBN + wave * (16 * kMxNB);
+  const int r0 = blockIdx.y * kMxBM + (wave >> 1) * (16 * kMxMI);
+  const int c0 = blockIdx.x * kMxBN + (wave & 1) * (16 * kMxNB);
   uint32_t arow[kMxMI], bcol[kMxNB];
 #pragma unroll
   for (int i = 0; i < kMxMI; ++i) arow[i] = (uint32_t)min(r0 + 16 * i + li, P.R - 1);
