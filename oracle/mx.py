@@ -94,3 +94,14 @@ def mx_gemm(W, N, K, X):
     xq = dequantize_mxfp8(*quantize_mxfp8(X))
     w = fm.dequantize("mxfp4", W, N, K)
     return xq @ w.T, np.abs(xq) @ np.abs(w).T
+
+
+def mx_expert_ffn(gbuf, ubuf, dbuf, H, F, X):
+    """One MXFP4/MXFP4 expert on the block-scaled path: g = W_g q(x),
+    u = W_u q(x), h = SiLU(g) u, o = W_d q(h), q = quantize_mxfp8 along the
+    inner dimension; returns o [R, H] and the bound sum_j |w_d[n, j] q(h)_j|.
+    Composed of mx_gemm and quantize_mxfp8 (pinned above) and SiLU."""
+    g, _ = mx_gemm(gbuf, F, H, X)
+    u, _ = mx_gemm(ubuf, F, H, X)
+    h = g / (1.0 + np.exp(-g)) * u
+    return mx_gemm(dbuf, H, F, h)
