@@ -357,6 +357,16 @@ def prefill_chunk(torch, calls=10):
             ("router_gemm", "topk", "permute", "prefill_prep", "prefill_gate_up",
              "prefill_down", "combine")}
     gemm_ms = kern["prefill_gate_up"] + kern["prefill_down"]
+    # the same chunk with the MXFP4 tier on the block-scaled matrix cores
+    for i in range(3):
+        layer.forward(x, i % 2, prefill=True, mx=True)
+    mx_ms = _events_ms(torch, lambda i: layer.forward(x, i % 2, prefill=True, mx=True), calls)
+    qmoe.profile_reset()
+    qmoe.profile_enable(True)
+    _events_ms(torch, lambda i: layer.forward(x, i % 2, prefill=True, mx=True), calls)
+    qmoe.profile_enable(False)
+    mx_kern = {k: qmoe.profile_read(k)[1] / calls for k in
+               ("prefill_mx_prep", "prefill_gate_up", "prefill_down")}
     del layer
     torch.cuda.empty_cache()
     log(f"prefill 2048 rows: {ms:.3f} ms per call (expert GEMMs {gemm_ms:.3f} ms)")
@@ -367,7 +377,9 @@ def prefill_chunk(torch, calls=10):
             "useful_gflop": round(flops / 1e9, 2),
             "mfma_util": round(flops / (gemm_ms * 1e-3) / 2.5e15, 4),
             "mfma_util_whole_call": round(flops / (ms * 1e-3) / 2.5e15, 4),
-            "kernel_ms": {k: round(v, 4) for k, v in kern.items()}}
+            "kernel_ms": {k: round(v, 4) for k, v in kern.items()},
+            "mx_tail_tier": {"ms_per_call": round(mx_ms, 4),
+                             "kernel_ms": {k: round(v, 4) for k, v in mx_kern.items()}}}
 
 
 def main():

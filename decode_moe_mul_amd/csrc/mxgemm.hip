@@ -16,25 +16,12 @@
 //    v_mfma_scale_f32_16x16x128_f8f6f4 per 16 x 16 output tile and 128 values
 //    of K (fp32 accumulation).
 //
-// Operand layout of that instruction (measured on the device with a one-wave
-// probe against a CPU model): lane l = 16 g + i supplies
-//  * B (FP4, 4 registers): column i, K values 32 g .. 32 g + 31 in nibble
-//    order (low nibble first): exactly unit g of the step in weight row i, so
-//    a lane loads one 16-byte unit of codes;
-//  * A (FP8, 8 registers): row i, K values 16 g .. 16 g + 15 (bytes 0..15)
-//    and 64 + 16 g .. 64 + 16 g + 15 (bytes 16..31);
-//  * scale bytes (byte 0 of a register): the scale of K block g (values
-//    32 g .. 32 g + 31) of its row (A) or column (B), whichever lanes hold
-//    that block's data;
-//  * result: rows 4 g .. 4 g + 3 of column i.
-#include "common.hpp"
+// The operand layout of that instruction is described in mx.hpp.
+#include "mx.hpp"
 
 #pragma clang fp contract(off)
 
 namespace qmoe {
-
-typedef int mx_v8i __attribute__((ext_vector_type(8)));
-typedef float mx_v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kMxWaves = 4;
 constexpr int kMxBlock = 64 * kMxWaves;
@@ -44,18 +31,6 @@ constexpr int kMxNB = 4;  // 16-column blocks per wave: 64 columns
 constexpr int kMxBM = 2 * 16 * kMxMI, kMxBN = 2 * 16 * kMxNB;
 
 // ------------------------------------------------ activation quantizer ----
-// |x| / 2^E (in [0, 512)) to the nearest E4M3 magnitude code, ties to even,
-// saturating at 448 (code 0x7E).  Exact: the subnormal range is an integer
-// multiple of 2^-9, the normal range keeps 3 of the 23 mantissa bits.
-QMOE_D uint32_t e4m3_code_of(float m) {
-  if (!(m < 448.f)) return 0x7Eu;
-  if (m < 0.015625f) return (uint32_t)__builtin_rintf(m * 512.f);  // 2^-6: subnormals
-  const uint32_t b = __builtin_bit_cast(uint32_t, m);
-  const uint32_t r = b + 0x7FFFFu + ((b >> 20) & 1u);  // round 23 -> 3 mantissa bits
-  const uint32_t code = ((((r >> 23) & 0xFFu) - 120u) << 3) | ((r >> 20) & 7u);
-  return code > 0x7Eu ? 0x7Eu : code;
-}
-
 __global__ __launch_bounds__(256) void quantize_act_mxfp8_kernel(const void* x, int x_dtype,
                                                                  int R, int K, uint8_t* codes,
                                                                  uint8_t* scales) {
@@ -84,29 +59,8 @@ __global__ __launch_bounds__(256) void quantize_act_mxfp8_kernel(const void* x, 
       }
     }
   }
-  float amax = 0.f;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  int e = 0;  // E8M0 byte
-  if (amax > 0.f) {
-    int ex;
-    frexpf(amax, &ex);  // amax = f * 2^ex, f in [0.5, 1)
-    e = min(max(127 + (ex - 1) - 8, 0), 254);
-  }
-  scales[blk] = (uint8_t)e;
   uint32_t out[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    uint32_t word = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float xv = v[4 * i + j];
-      uint32_t c = e4m3_code_of(ldexpf(fabsf(xv), 127 - e));
-      if (xv < 0.f) c |= 0x80u;
-      word |= c << (8 * j);
-    }
-    out[i] = word;
-  }
+  scales[blk] = (uint8_t)mx_quantize32(v, out);
   uint4* dst = (uint4*)(codes + at);
   dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
   dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
@@ -169,17 +123,10 @@ __global__ __launch_bounds__(kMxBlock) void mxfp4_gemm_kernel(MxParams P) {
     for (int b = 0; b < kMxNB; ++b) acc[i][b] = mx_v4f{0.f, 0.f, 0.f, 0.f};
   auto mma = [&](const MxA (&a)[kMxMI], const MxB (&w)[kMxNB]) {
 #pragma unroll
-    for (int i = 0; i < kMxMI; ++i) {
-      const mx_v8i av = {(int)a[i].lo.x, (int)a[i].lo.y, (int)a[i].lo.z, (int)a[i].lo.w,
-                         (int)a[i].hi.x, (int)a[i].hi.y, (int)a[i].hi.z, (int)a[i].hi.w};
+    for (int i = 0; i < kMxMI; ++i)
 #pragma unroll
-      for (int b = 0; b < kMxNB; ++b) {
-        const mx_v8i bv = {(int)w[b].q.x, (int)w[b].q.y, (int)w[b].q.z, (int)w[b].q.w, 0, 0, 0, 0};
-        acc[i][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            av, bv, acc[i][b], 0 /* A: FP8 E4M3 */, 4 /* B: FP4 E2M1 */, 0, (int)a[i].s, 0,
-            (int)w[b].s);
-      }
-    }
+      for (int b = 0; b < kMxNB; ++b)
+        acc[i][b] = mx_mma(a[i].lo, a[i].hi, a[i].s, w[b].q, w[b].s, acc[i][b]);
   };
   MxA a0[kMxMI], a1[kMxMI];
   MxB w0[kMxNB], w1[kMxNB];

@@ -33,7 +33,7 @@
 // Activations and h are fp16 (11-bit significands) inside the products.
 #include <algorithm>
 
-#include "common.hpp"
+#include "mx.hpp"
 
 #pragma clang fp contract(off)
 
@@ -64,6 +64,14 @@ struct PrefillParams {
   int xs, hs;            // row strides: H and F rounded up to whole K steps
   float* o;              // [T*k, H]
   int ntiles;            // column tiles of this pass
+  // block-scaled path (qgemm_grouped_prefill_mx): tiers whose gate/up and
+  // down are both MXFP4 read MXFP8 activations: x8 [T + 1, xs] and h8
+  // [T*k + 1, hs] E4M3 bytes (last rows and padding zero) with E8M0 scales
+  // x8s [T + 1, xs / 32], h8s [T*k + 1, hs / 32]
+  const uint8_t* x8;
+  const uint8_t* x8s;
+  uint8_t* h8;
+  uint8_t* h8s;
 };
 
 // The tier holding expert e, assembled field by field with constant indices
@@ -327,6 +335,9 @@ QMOE_D void tile_gemm(const PrefillParams& P, const void* W0, const void* W1, in
   load_a(0, ra0);
   load_b(min(1, last), rb1);
   load_a(min(1, last), ra1);
+  // the block's previous item may still be reading LDS buffer 0 (its last
+  // step, when the step count is odd)
+  __syncthreads();
   write_a(0, ra0);
   load_a(min(2, last), ra0);
   __syncthreads();
@@ -370,6 +381,132 @@ QMOE_D void tile_gemm(const PrefillParams& P, const void* W0, const void* W1, in
   }
 }
 
+// One tile of an MXFP4/MXFP4 tier on the block-scaled matrix cores: rows
+// pos0 .. pos0 + cnt - 1 x the pass's column tile nt.  Weights are used as
+// stored (lane (n, g) loads unit g of the step in row n, 16 bytes, and its
+// E8M0 byte); activations are the MXFP8 rows x8 (pass 1, gathered by token)
+// or h8 (pass 2, by position), loaded straight from global memory; rows past
+// the tile read the zero row.  Row groups are taken 4 at a time (64 rows), so
+// a 128-row tile streams its weights twice (the second time from the caches).
+// Pass 1 writes h = SiLU(g) * u through the LDS tile hl [16 MI][64] and
+// quantizes each row's two 32-column blocks to MXFP8 into h8 / h8s.
+template <int PASS, int NB, int MI>
+QMOE_D void tile_mx(const PrefillParams& P, const void* W0, const void* W1, int pos0, int cnt,
+                    int nt, float* hl) {
+  static_assert(PASS != 1 || NB == 1, "the gate/up epilogue assumes 16 columns per wave");
+  constexpr int NMAT = PASS == 1 ? 2 : 1;
+  constexpr int SMI = MI < 4 ? MI : 4;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int li = lane & 15, g = lane >> 4;
+  const int N = PASS == 1 ? P.F : P.H, K = PASS == 1 ? P.H : P.F;
+  const int U = K >> 5, nsteps = (U + 3) >> 2;
+  const int n0 = nt * (kPW * NB * 16) + wave * (NB * 16);
+  Planes mats[NMAT];
+  mats[0] = planes_of(W0, QMOE_MXFP4, N, K);
+  if constexpr (NMAT == 2) mats[1] = planes_of(W1, QMOE_MXFP4, N, K);
+  uint32_t wrow[NB];  // weight rows past N re-read row N - 1 (never stored)
+#pragma unroll
+  for (int b = 0; b < NB; ++b) wrow[b] = (uint32_t)min(n0 + 16 * b + li, N - 1);
+  const uint32_t astride = (uint32_t)(PASS == 1 ? P.xs : P.hs), sstride = astride >> 5;
+  const uint8_t* abase = PASS == 1 ? P.x8 : P.h8;
+  const uint8_t* sbase = PASS == 1 ? P.x8s : P.h8s;
+  const int zero_row = PASS == 1 ? P.T : P.T * P.k;
+  const int nmi = (cnt + 15) >> 4;  // block-uniform
+  const int last = nsteps - 1;
+  __syncthreads();  // the block's previous item may still be reading the LDS tile
+  struct A8 { uint4 lo, hi; uint32_t s; };
+  struct B4 { uint4 q; uint32_t s; };
+  for (int gi0 = 0; gi0 < nmi; gi0 += SMI) {
+    uint32_t arow[SMI];
+#pragma unroll
+    for (int i = 0; i < SMI; ++i) {
+      const int r = 16 * (gi0 + i) + li;
+      arow[i] = (uint32_t)(r < cnt ? (PASS == 1 ? P.perm[pos0 + r] / P.k : pos0 + r) : zero_row);
+    }
+    auto load = [&](int st, A8 (&a)[SMI], B4 (&w)[NB][NMAT]) {
+      const uint32_t k0 = (uint32_t)st * 128u, ab = (uint32_t)st * 4u + (uint32_t)g;
+      const uint32_t u = (uint32_t)min(st * 4 + g, U - 1);  // units past K meet zero rows
+#pragma unroll
+      for (int i = 0; i < SMI; ++i) {
+        const uint8_t* row = abase + arow[i] * astride + k0;
+        a[i].lo = *(const uint4*)(row + 16u * g);
+        a[i].hi = *(const uint4*)(row + 64u + 16u * g);
+        a[i].s = sbase[arow[i] * sstride + ab];
+      }
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) {
+          w[b][m].q = *(const uint4*)(mats[m].p0 + wrow[b] * (uint32_t)(K >> 1) + 16u * u);
+          w[b][m].s = mats[m].p1[wrow[b] * (uint32_t)U + u];
+        }
+    };
+    mx_v4f acc[NMAT][NB][SMI];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int i = 0; i < SMI; ++i) acc[m][b][i] = mx_v4f{0.f, 0.f, 0.f, 0.f};
+    auto mma = [&](const A8 (&a)[SMI], const B4 (&w)[NB][NMAT]) {
+#pragma unroll
+      for (int i = 0; i < SMI; ++i)
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int m = 0; m < NMAT; ++m)
+            acc[m][b][i] = mx_mma(a[i].lo, a[i].hi, a[i].s, w[b][m].q, w[b][m].s, acc[m][b][i]);
+    };
+    A8 a0[SMI], a1[SMI];
+    B4 w0[NB][NMAT], w1[NB][NMAT];
+    load(0, a0, w0);
+    int st = 0;
+    for (; st + 1 < nsteps; st += 2) {
+      load(st + 1, a1, w1);
+      mma(a0, w0);
+      load(min(st + 2, last), a0, w0);
+      mma(a1, w1);
+    }
+    if (st < nsteps) mma(a0, w0);
+    // lane holds rows 16 (gi0 + i) + 4 g + j of column n0 + 16 b + li
+#pragma unroll
+    for (int i = 0; i < SMI; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 16 * (gi0 + i) + 4 * g + j;
+        if (r >= cnt) continue;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const int col = n0 + 16 * b + li;
+          if constexpr (PASS == 1) {
+            const float gv = acc[0][b][i][j], uv = acc[1][b][i][j];
+            hl[r * 64 + wave * 16 + li] = gv / (1.f + expf(-gv)) * uv;
+          } else {
+            if (col < N) P.o[(size_t)(pos0 + r) * N + col] = acc[0][b][i][j];
+          }
+        }
+      }
+  }
+  if constexpr (PASS == 1) {
+    // quantize the tile's h rows: thread t takes row t >> 1, 32-column half t & 1
+    __syncthreads();
+    const int r = threadIdx.x >> 1, half = threadIdx.x & 1;
+    if (r < cnt) {
+      float v[32];
+#pragma unroll
+      for (int j = 0; j < 32; ++j) v[j] = hl[r * 64 + 32 * half + j];
+      uint32_t out[8];
+      const uint32_t e = mx_quantize32(v, out);
+      const size_t pos = (size_t)(pos0 + r);
+      uint4* dst = (uint4*)(P.h8 + pos * P.hs + nt * 64 + 32 * half);
+      dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
+      dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
+      P.h8s[pos * (P.hs >> 5) + nt * 2 + half] = (uint8_t)e;
+    }
+    __syncthreads();  // the LDS tile is reused by the next item
+  }
+}
+
 // Tiles of more than kSmall rows (up to kBM) and tiles of at most kSmall
 // rows run in separate launches: each kernel's registers and LDS are sized
 // for its own tile height, so the short tiles (experts with a few rows,
@@ -390,7 +527,9 @@ QMOE_D void tile_dispatch_full(const PrefillParams& P, const void* W0, const voi
 // (tile, column tile) items.  Item w runs on XCD w & 7 (the grid is a multiple
 // of 8); the column tiles of one row tile share an XCD and follow each other
 // there, so its staged activation rows are read from that XCD's L2.
-template <int PASS, int NB, int MI>
+// MXP: MXFP4/MXFP4 tiers take the block-scaled path (instantiated apart, so
+// the plain kernels keep their registers).
+template <int PASS, int NB, int MI, bool MXP>
 __global__ __launch_bounds__(kPB, MI == kMIsmall ? 3 : 2) void prefill_kernel(PrefillParams P, int list) {
   __shared__ __align__(16) uint16_t As[2 * 16 * MI * kAS];
   const int2* tiles = P.tiles + (list ? P.tiles_cap_big : 0);
@@ -415,7 +554,15 @@ __global__ __launch_bounds__(kPB, MI == kMIsmall ? 3 : 2) void prefill_kernel(Pr
     switch (fmt) {
       case QMOE_Q8_0: tile_dispatch_full<QMOE_Q8_0, PASS, NB, MI>(P, W0, W1, pos0, cnt, nt, As); break;
       case QMOE_Q4_0: tile_dispatch_full<QMOE_Q4_0, PASS, NB, MI>(P, W0, W1, pos0, cnt, nt, As); break;
-      case QMOE_MXFP4: tile_dispatch_full<QMOE_MXFP4, PASS, NB, MI>(P, W0, W1, pos0, cnt, nt, As); break;
+      case QMOE_MXFP4:
+        if constexpr (MXP) {
+          if (t.fmt_gate_up == QMOE_MXFP4 && t.fmt_down == QMOE_MXFP4) {
+            tile_mx<PASS, NB, MI>(P, W0, W1, pos0, cnt, nt, (float*)As);
+            break;
+          }
+        }
+        tile_dispatch_full<QMOE_MXFP4, PASS, NB, MI>(P, W0, W1, pos0, cnt, nt, As);
+        break;
       case QMOE_Q4_K: tile_dispatch_full<QMOE_Q4_K, PASS, NB, MI>(P, W0, W1, pos0, cnt, nt, As); break;
       case QMOE_Q6_K: tile_dispatch_full<QMOE_Q6_K, PASS, NB, MI>(P, W0, W1, pos0, cnt, nt, As); break;
       default: break;
@@ -511,6 +658,51 @@ __global__ __launch_bounds__(kPB) void prefill_prep_kernel(const int32_t* offset
   }
 }
 
+// Block-scaled path: x (fp32 or bf16) [T, H] -> MXFP8 x8 [T + 1, xs] and
+// x8s [T + 1, xs / 32] (32-value blocks past H and the last row: zero codes,
+// scale byte 0), and zero codes / scales in h8's last row and its blocks
+// past F.  One thread per 32-value block.
+__global__ __launch_bounds__(kPB) void prefill_mx_prep_kernel(const void* x, int x_dtype, int T,
+                                                              int H, int xs, uint8_t* x8,
+                                                              uint8_t* x8s, int A, int F, int hs,
+                                                              uint8_t* h8, uint8_t* h8s) {
+  const long long xb = (long long)(T + 1) * (xs / 32);
+  const int pb = (hs - F) / 32;                     // pad blocks per h8 row
+  const long long hb = (long long)A * pb + hs / 32;  // pads, then the last row
+  const long long i = (long long)blockIdx.x * kPB + threadIdx.x;
+  if (i >= xb + hb) return;
+  uint32_t out[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+  uint32_t e = 0;
+  uint8_t* codes;
+  uint8_t* scale;
+  if (i < xb) {
+    const long long row = i / (xs / 32);
+    const int blk = (int)(i - row * (xs / 32));
+    if (row < T && 32 * blk < H) {
+      float v[32];
+      const long long at = row * H + 32 * blk;
+#pragma unroll
+      for (int j = 0; j < 32; ++j)
+        v[j] = x_dtype == QMOE_F32 ? ((const float*)x)[at + j]
+                                   : bf16_bits_to_f32(((const uint16_t*)x)[at + j]);
+      e = mx_quantize32(v, out);
+    }
+    codes = x8 + row * xs + 32 * blk;
+    scale = x8s + row * (xs / 32) + blk;
+  } else {
+    const long long j = i - xb;
+    const long long pad = (long long)A * pb;
+    const long long row = j < pad ? j / pb : A;
+    const int blk = j < pad ? F / 32 + (int)(j % pb) : (int)(j - pad);
+    codes = h8 + row * hs + 32 * blk;
+    scale = h8s + row * (hs / 32) + blk;
+  }
+  uint4* dst = (uint4*)codes;
+  dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
+  dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
+  *scale = (uint8_t)e;
+}
+
 // Activation row strides: whole K steps.
 QMOE_HD int step_round(int K) { return (K + kBK - 1) / kBK * kBK; }
 
@@ -536,46 +728,71 @@ static int persistent_grid(Kernel kernel) {
 
 int validate_tiers(const qmoe_tier* tiers, int n_tiers, int E, int H, int F, bool prefill);
 
-}  // namespace qmoe
+// Workspace: fp16 h and x, the tile lists, then the MXFP8 rows and scales of
+// x and h (used by the block-scaled path only).
+static size_t mx_bytes(long long rows, int stride) {
+  return round_up256((size_t)rows * stride) + round_up256((size_t)rows * (stride / 32));
+}
 
-using namespace qmoe;
-
-extern "C" {
-
-size_t qgemm_grouped_prefill_workspace_size(int T, int k, int E, int H, int F) {
+static size_t prefill_workspace_bytes(int T, int k, int E, int H, int F) {
   if (T < 0 || k < 0 || E <= 0 || H < 0 || F < 0) return 0;
   const long long A = (long long)T * k;
   return round_up256((size_t)(A + 1) * step_round(F) * sizeof(uint16_t)) +
          round_up256((size_t)(T + 1) * step_round(H) * sizeof(uint16_t)) +
          round_up256((size_t)(prefill_cap_big(A) + prefill_cap_small(A, E)) * sizeof(int2)) +
-         256 + 256;
+         256 + 256 + mx_bytes(T + 1, step_round(H)) + mx_bytes(A + 1, step_round(F));
 }
 
-int qgemm_grouped_prefill(const qmoe_tier* tiers, int n_tiers, int E, int H, int F,
-                          const void* x, int x_dtype, int T, int k, const int32_t* offsets,
-                          const int32_t* perm, float* o, void* ws, size_t ws_bytes,
-                          void* stream) {
+// per pass: the big-tile list, then the small-tile list
+template <bool MXP>
+static int prefill_launch(PrefillParams P, hipStream_t s) {
+  static int grid[2][2] = {{0, 0}, {0, 0}};
+  if (!grid[0][0]) {
+    grid[0][0] = persistent_grid(prefill_kernel<1, kNB1, kMI, MXP>);
+    grid[0][1] = persistent_grid(prefill_kernel<1, kNB1, kMIsmall, MXP>);
+    grid[1][0] = persistent_grid(prefill_kernel<2, kNB2, kMI, MXP>);
+    grid[1][1] = persistent_grid(prefill_kernel<2, kNB2, kMIsmall, MXP>);
+  }
+  P.ntiles = (P.F + kPW * kNB1 * 16 - 1) / (kPW * kNB1 * 16);
+  int st = QMOE_LAUNCH("prefill_gate_up", (prefill_kernel<1, kNB1, kMI, MXP>), dim3(grid[0][0]),
+                       kPB, 0, s, P, 0);
+  if (st) return st;
+  st = QMOE_LAUNCH("prefill_gate_up", (prefill_kernel<1, kNB1, kMIsmall, MXP>),
+                   dim3(grid[0][1]), kPB, 0, s, P, 1);
+  if (st) return st;
+  P.ntiles = (P.H + kPW * kNB2 * 16 - 1) / (kPW * kNB2 * 16);
+  st = QMOE_LAUNCH("prefill_down", (prefill_kernel<2, kNB2, kMI, MXP>), dim3(grid[1][0]), kPB, 0,
+                   s, P, 0);
+  if (st) return st;
+  return QMOE_LAUNCH("prefill_down", (prefill_kernel<2, kNB2, kMIsmall, MXP>), dim3(grid[1][1]),
+                     kPB, 0, s, P, 1);
+}
+
+static int prefill_run(const char* who, bool mx, const qmoe_tier* tiers, int n_tiers, int E,
+                       int H, int F, const void* x, int x_dtype, int T, int k,
+                       const int32_t* offsets, const int32_t* perm, float* o, void* ws,
+                       size_t ws_bytes, void* stream) {
   if (T < 0 || k < 0)
-    return fail(QMOE_ERR_INVALID_ARG, "qgemm_grouped_prefill: T=%d k=%d", T, k);
+    return fail(QMOE_ERR_INVALID_ARG, "%s: T=%d k=%d", who, T, k);
   if (T == 0 || k == 0) return QMOE_OK;
   int st = validate_tiers(tiers, n_tiers, E, H, F, true);
   if (st) return st;
-  if (E > 8192) return fail(QMOE_ERR_UNSUPPORTED, "qgemm_grouped_prefill: E=%d > 8192", E);
+  if (E > 8192) return fail(QMOE_ERR_UNSUPPORTED, "%s: E=%d > 8192", who, E);
   if (H % 64 || F % 64)
-    return fail(QMOE_ERR_INVALID_ARG, "qgemm_grouped_prefill: H and F must be multiples of 64");
+    return fail(QMOE_ERR_INVALID_ARG, "%s: H and F must be multiples of 64", who);
   if ((long long)H * F >= (1LL << 32))  // plane offsets are 32-bit
-    return fail(QMOE_ERR_UNSUPPORTED, "qgemm_grouped_prefill: H*F too large");
+    return fail(QMOE_ERR_UNSUPPORTED, "%s: H*F too large", who);
   if (!x || !offsets || !perm || !o)
-    return fail(QMOE_ERR_INVALID_ARG, "qgemm_grouped_prefill: null pointer");
+    return fail(QMOE_ERR_INVALID_ARG, "%s: null pointer", who);
   if (x_dtype != QMOE_F32 && x_dtype != QMOE_BF16)
-    return fail(QMOE_ERR_UNSUPPORTED, "qgemm_grouped_prefill: unknown x_dtype %d", x_dtype);
+    return fail(QMOE_ERR_UNSUPPORTED, "%s: unknown x_dtype %d", who, x_dtype);
   if (!QMOE_ALIGNED(x, 16) || !QMOE_ALIGNED(o, 16))
-    return fail(QMOE_ERR_INVALID_ARG, "qgemm_grouped_prefill: misaligned x/o");
-  const size_t need = qgemm_grouped_prefill_workspace_size(T, k, E, H, F);
+    return fail(QMOE_ERR_INVALID_ARG, "%s: misaligned x/o", who);
+  const size_t need = prefill_workspace_bytes(T, k, E, H, F);
   if (!ws || ws_bytes < need || !QMOE_ALIGNED(ws, 256))
-    return fail(QMOE_ERR_WORKSPACE, "qgemm_grouped_prefill: workspace %zu < %zu", ws_bytes, need);
+    return fail(QMOE_ERR_WORKSPACE, "%s: workspace %zu < %zu", who, ws_bytes, need);
   const long long A = (long long)T * k;
-  if (A > (1 << 24)) return fail(QMOE_ERR_UNSUPPORTED, "qgemm_grouped_prefill: T*k too large");
+  if (A > (1 << 24)) return fail(QMOE_ERR_UNSUPPORTED, "%s: T*k too large", who);
   hipStream_t s = (hipStream_t)stream;
   PrefillParams P{};
   for (int i = 0; i < n_tiers; ++i) P.tiers[i] = tiers[i];
@@ -595,33 +812,56 @@ int qgemm_grouped_prefill(const qmoe_tier* tiers, int n_tiers, int E, int H, int
   int2* tiles = (int2*)w;
   P.tiles = tiles;
   P.tiles_cap_big = (int)prefill_cap_big(A);
+  w += round_up256((size_t)(prefill_cap_big(A) + prefill_cap_small(A, E)) * sizeof(int2));
+  uint8_t* x8 = (uint8_t*)w;
+  P.x8 = x8;
+  w += round_up256((size_t)(T + 1) * P.xs);
+  uint8_t* x8s = (uint8_t*)w;
+  P.x8s = x8s;
+  w += round_up256((size_t)(T + 1) * (P.xs / 32));
+  P.h8 = (uint8_t*)w;
+  w += round_up256((size_t)(A + 1) * P.hs);
+  P.h8s = (uint8_t*)w;
   const long long chunks = (long long)(T + 1) * (P.xs / 8) + A * ((P.hs - F) / 8) + P.hs / 8;
   const long long conv_blocks = std::min<long long>(1024, (chunks + kPB - 1) / kPB);
   st = QMOE_LAUNCH("prefill_prep", prefill_prep_kernel, dim3((unsigned)(1 + conv_blocks)), kPB, 0,
                    s, offsets, E, P.tiles_cap_big, tiles, counts, x, x_dtype, T, H, P.xs, x16,
                    (int)A, F, P.hs, P.h);
   if (st) return st;
-  // per pass: the big-tile list, then the small-tile list
-  static int grid[2][2] = {{0, 0}, {0, 0}};
-  if (!grid[0][0]) {
-    grid[0][0] = persistent_grid(prefill_kernel<1, kNB1, kMI>);
-    grid[0][1] = persistent_grid(prefill_kernel<1, kNB1, kMIsmall>);
-    grid[1][0] = persistent_grid(prefill_kernel<2, kNB2, kMI>);
-    grid[1][1] = persistent_grid(prefill_kernel<2, kNB2, kMIsmall>);
+  if (mx) {
+    const long long blocks = (long long)(T + 1) * (P.xs / 32) + A * ((P.hs - F) / 32) + P.hs / 32;
+    st = QMOE_LAUNCH("prefill_mx_prep", prefill_mx_prep_kernel,
+                     dim3((unsigned)((blocks + kPB - 1) / kPB)), kPB, 0, s, x, x_dtype, T, H,
+                     P.xs, x8, x8s, (int)A, F, P.hs, P.h8, P.h8s);
+    if (st) return st;
   }
-  P.ntiles = (F + kPW * kNB1 * 16 - 1) / (kPW * kNB1 * 16);
-  st = QMOE_LAUNCH("prefill_gate_up", (prefill_kernel<1, kNB1, kMI>), dim3(grid[0][0]), kPB, 0, s,
-                   P, 0);
-  if (st) return st;
-  st = QMOE_LAUNCH("prefill_gate_up", (prefill_kernel<1, kNB1, kMIsmall>), dim3(grid[0][1]), kPB,
-                   0, s, P, 1);
-  if (st) return st;
-  P.ntiles = (H + kPW * kNB2 * 16 - 1) / (kPW * kNB2 * 16);
-  st = QMOE_LAUNCH("prefill_down", (prefill_kernel<2, kNB2, kMI>), dim3(grid[1][0]), kPB, 0, s,
-                   P, 0);
-  if (st) return st;
-  return QMOE_LAUNCH("prefill_down", (prefill_kernel<2, kNB2, kMIsmall>), dim3(grid[1][1]), kPB, 0,
-                     s, P, 1);
+  return mx ? prefill_launch<true>(P, s) : prefill_launch<false>(P, s);
+}
+
+}  // namespace qmoe
+
+using namespace qmoe;
+
+extern "C" {
+
+size_t qgemm_grouped_prefill_workspace_size(int T, int k, int E, int H, int F) {
+  return prefill_workspace_bytes(T, k, E, H, F);
+}
+
+int qgemm_grouped_prefill(const qmoe_tier* tiers, int n_tiers, int E, int H, int F,
+                          const void* x, int x_dtype, int T, int k, const int32_t* offsets,
+                          const int32_t* perm, float* o, void* ws, size_t ws_bytes,
+                          void* stream) {
+  return prefill_run("qgemm_grouped_prefill", false, tiers, n_tiers, E, H, F, x, x_dtype, T, k,
+                     offsets, perm, o, ws, ws_bytes, stream);
+}
+
+int qgemm_grouped_prefill_mx(const qmoe_tier* tiers, int n_tiers, int E, int H, int F,
+                             const void* x, int x_dtype, int T, int k, const int32_t* offsets,
+                             const int32_t* perm, float* o, void* ws, size_t ws_bytes,
+                             void* stream) {
+  return prefill_run("qgemm_grouped_prefill_mx", true, tiers, n_tiers, E, H, F, x, x_dtype, T,
+                     k, offsets, perm, o, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

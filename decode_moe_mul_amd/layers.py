@@ -129,11 +129,13 @@ class MoELayer:
         return (not prefill and T <= 16 and c.E <= 512
                 and ((T * kt + 63) // 64) * 64 + 16 + c.E_total <= 8192)
 
-    def forward(self, x, copy=0, prefill=False, one_launch=False):
+    def forward(self, x, copy=0, prefill=False, one_launch=False, mx=False):
         """y [T, H] for activations x [T, H] (float32 or bfloat16).  The
         intermediate ids, p, offsets, perm, inv (and o, unless one_launch)
         stay in the workspace dict returned second.  one_launch: the whole
-        decode layer as moe_layer_decode (T <= 16)."""
+        decode layer as moe_layer_decode (T <= 16).  mx (with prefill): the
+        MXFP4/MXFP4 tiers on the block-scaled matrix cores
+        (qgemm_grouped_prefill_mx)."""
         c = self.cfg
         T = x.shape[0]
         ws = self.workspaces(T, prefill)
@@ -163,7 +165,8 @@ class MoELayer:
             qmoe._check(L.moe_permute(qmoe._p(ws["ids"]), T, kt, c.E_total,
                                       qmoe._p(ws["offsets"]), qmoe._p(ws["perm"]),
                                       qmoe._p(ws["inv"]), s), "moe_permute")
-        fn = L.qgemm_grouped_prefill if prefill else L.moe_ffn_tiered
+        fn = ((L.qgemm_grouped_prefill_mx if mx else L.qgemm_grouped_prefill) if prefill
+              else L.moe_ffn_tiered)
         arr = self.tier_arrays[copy]
         qmoe._check(fn(arr, len(arr), c.E_total, c.H, c.F, qmoe._p(x), qmoe._dtype_code(x), T, kt,
                        qmoe._p(ws["offsets"]), qmoe._p(ws["perm"]), qmoe._p(ws["o"]),

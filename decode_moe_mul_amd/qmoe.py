@@ -60,6 +60,8 @@ _SIGNATURES = {
     "qgemm_grouped_prefill_workspace_size": (_SZ, [_I, _I, _I, _I, _I]),
     "qgemm_grouped_prefill": (_I, [ctypes.POINTER(Tier), _I, _I, _I, _I, _VP, _I, _I, _I, _VP,
                                    _VP, _VP, _VP, _SZ, _VP]),
+    "qgemm_grouped_prefill_mx": (_I, [ctypes.POINTER(Tier), _I, _I, _I, _I, _VP, _I, _I, _I, _VP,
+                                      _VP, _VP, _VP, _SZ, _VP]),
     "moe_combine": (_I, [_VP, _VP, _VP, _I, _I, _I, _VP, _VP, _VP]),
     "qquantize_act_mxfp8": (_I, [_VP, _I, _I, _I, _VP, _VP, _VP]),
     "qgemm_mxfp4_mxfp8": (_I, [_VP, _I, _I, _VP, _VP, _I, _VP, _VP]),
@@ -339,6 +341,14 @@ def grouped_prefill(tiers, E, H, F, x, k, offsets, perm, out=None, ws=None):
     if ws is None:
         ws = prefill_workspace(x.shape[0], k, E, H, F, x.device)
     return _ffn_call("qgemm_grouped_prefill", tiers, E, H, F, x, k, offsets, perm, out, ws)
+
+
+def grouped_prefill_mx(tiers, E, H, F, x, k, offsets, perm, out=None, ws=None):
+    """As grouped_prefill, with MXFP4/MXFP4 tiers on the block-scaled matrix
+    cores against MXFP8 activations."""
+    if ws is None:
+        ws = prefill_workspace(x.shape[0], k, E, H, F, x.device)
+    return _ffn_call("qgemm_grouped_prefill_mx", tiers, E, H, F, x, k, offsets, perm, out, ws)
 
 
 def combine(o, inv_perm, p, T, k, H, shared=None, out=None):

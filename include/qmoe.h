@@ -282,12 +282,25 @@ int moe_ffn_tiered(const qmoe_tier *tiers, int n_tiers, int E, int H, int F,
  * fp16 between the gate/up pass and the down pass.  Same arguments as
  * moe_ffn_tiered; H and F must be multiples of 64.
  * Workspace: qgemm_grouped_prefill_workspace_size(T, k, E, H, F) bytes:
- * h [T*k, F] fp16, x [T, H] fp16 and the tile table.                        */
+ * h [T*k, F] fp16, x [T, H] fp16, the tile table, and the MXFP8 copies of x
+ * and h used by qgemm_grouped_prefill_mx.                                   */
 size_t qgemm_grouped_prefill_workspace_size(int T, int k, int E, int H, int F);
 int qgemm_grouped_prefill(const qmoe_tier *tiers, int n_tiers, int E, int H,
                           int F, const void *x, int x_dtype, int T, int k,
                           const int32_t *offsets, const int32_t *perm, float *o,
                           void *ws, size_t ws_bytes, void *stream);
+
+/* qgemm_grouped_prefill_mx: qgemm_grouped_prefill, except that every tier
+ * whose gate/up and down are both MXFP4 runs on the gfx950 block-scaled matrix
+ * cores ([P1] "NInfer 80 SM port", list of hardware limits): its weights are
+ * used as stored, x is quantized to MXFP8 as qquantize_act_mxfp8 does, and
+ * h = SiLU(g) * u (fp32 from the matrix cores) is quantized the same way
+ * along F before the down projection.  Other tiers give the same o as
+ * qgemm_grouped_prefill, bit for bit.  Same arguments and workspace.        */
+int qgemm_grouped_prefill_mx(const qmoe_tier *tiers, int n_tiers, int E, int H,
+                             int F, const void *x, int x_dtype, int T, int k,
+                             const int32_t *offsets, const int32_t *perm,
+                             float *o, void *ws, size_t ws_bytes, void *stream);
 
 /* moe_combine: y[t, :] = sum_{i<k} p[t, i] * o[inv_perm[t*k + i], :]
  *                        + shared[t, :]
