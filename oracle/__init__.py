@@ -15,6 +15,8 @@ path computes, in float64 NumPy:
   routed-expert layer, and the per-element error bounds used for parity.
 * ``oracle.mx``       -- MXFP8 (E4M3) activation quantization and the MX GEMM
   reference for MXFP4 weights on block-scaled matrix cores.
+* ``oracle.int8``     -- int8 activation quantization and the Q8_0 x int8
+  GEMV reference (integer dot products).
 * ``oracle.brute``    -- pure-Python scalar loops for tiny cases, used only to
   cross-check the vectorised oracle.
 
