@@ -291,6 +291,52 @@ def ternary_gemv(torch, steps):
     return res
 
 
+def int8_gemv(torch, calls=50):
+    """The Llama-3-8B layer's seven matrices in Q8_0 at 1 and 16 decode rows:
+    qgemv_q8_0 on fp32 activations against qquantize_act_q8 + qgemv_q8_0_i8
+    (int8 activations, v_dot4 integer dot products), 4 weight copies
+    rotated."""
+    from decode_moe_mul_amd import configs, qmoe, synth
+    mats = [(n, N, K) for (n, N, K, _) in configs.LLAMA8B_GEMV.mats]
+    copies = 4
+    bufs = []
+    for c in range(copies):
+        row = []
+        for i, (n, N, K) in enumerate(mats):
+            W = synth.normal_device((N, K), 0.02, 9, synth.GATE, 100 * c + i, "cuda")
+            row.append(qmoe.quantize("q8_0", W))
+            del W
+        bufs.append(row)
+    nbytes = sum(qmoe.tensor_bytes("q8_0", N, K) for _, N, K in mats)
+    out = {"workload": "llama3_8b_layer_gemv in Q8_0 x7", "weight_bytes": int(nbytes)}
+    for R in (1, 16):
+        xs = {K: torch.from_numpy(synth.normal((R, K), 1.0, 4, synth.ACT, K)).cuda()
+              for K in {K for _, _, K in mats}}
+        ys = [torch.empty((R, N), dtype=torch.float32, device="cuda") for _, N, _ in mats]
+
+        def fp_call(i):
+            for j, (n, N, K) in enumerate(mats):
+                qmoe.gemv("q8_0", bufs[i % copies][j], N, K, xs[K], out=ys[j])
+
+        def i8_call(i):
+            qs = {K: qmoe.quantize_act_q8(x) for K, x in xs.items()}
+            for j, (n, N, K) in enumerate(mats):
+                q, d = qs[K]
+                qmoe.gemv_q8_0_i8(bufs[i % copies][j], N, K, q, d, out=ys[j])
+
+        fp_call(0), i8_call(0)
+        fms = _events_ms(torch, fp_call, calls)
+        ims = _events_ms(torch, i8_call, calls)
+        out[f"rows_{R}"] = {"fp_act_us": round(fms * 1e3, 2),
+                            "fp_act_gbs": round(nbytes / (fms * 1e-3) / 1e9, 1),
+                            "int8_act_us": round(ims * 1e3, 2),
+                            "int8_act_gbs": round(nbytes / (ims * 1e-3) / 1e9, 1)}
+    del bufs
+    torch.cuda.empty_cache()
+    log(f"int8 gemv: {out}")
+    return out
+
+
 def mx_gemm(torch, calls=20):
     """MXFP4 weights x MXFP8 activations on the block-scaled matrix cores
     (qgemm_mxfp4_mxfp8) for 2048 activation rows: the tail tier's expert
@@ -492,6 +538,7 @@ def main():
     ternary = None if a.decode_only else ternary_gemv(torch, a.steps)
     prefill = None if a.decode_only else prefill_chunk(torch)
     mx = None if a.decode_only else mx_gemm(torch)
+    i8 = None if a.decode_only else int8_gemv(torch)
 
     t = stored_traffic()
     traffic = None if t is None else int(t["traffic_bytes_per_launch"])
@@ -539,6 +586,8 @@ def main():
         out["prefill"] = prefill
     if mx is not None:
         out["mx_gemm"] = mx
+    if i8 is not None:
+        out["int8_gemv"] = i8
     if not a.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         out["cpu_baseline"] = cpu_baseline()

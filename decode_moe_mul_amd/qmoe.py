@@ -64,6 +64,8 @@ _SIGNATURES = {
                                       _VP, _VP, _VP, _SZ, _VP]),
     "moe_combine": (_I, [_VP, _VP, _VP, _I, _I, _I, _VP, _VP, _VP]),
     "qquantize_act_mxfp8": (_I, [_VP, _I, _I, _I, _VP, _VP, _VP]),
+    "qquantize_act_q8": (_I, [_VP, _I, _I, _I, _VP, _VP, _VP]),
+    "qgemv_q8_0_i8": (_I, [_VP, _I, _I, _VP, _VP, _I, _VP, _VP]),
     "qgemm_mxfp4_mxfp8": (_I, [_VP, _I, _I, _VP, _VP, _I, _VP, _VP]),
     "moe_layer_decode_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "moe_layer_decode": (_I, [ctypes.POINTER(Tier), _I, _I, _I, _I, _VP, _I, _I, _VP, _VP, _I,
@@ -372,6 +374,31 @@ def quantize_act_mxfp8(x):
     _check(lib().qquantize_act_mxfp8(_p(x), _dtype_code(x), R, K, _p(codes), _p(scales),
                                      _stream()), "qquantize_act_mxfp8")
     return codes, scales
+
+
+def quantize_act_q8(x):
+    """Activations [R, K] (float32 or bfloat16) -> int8 codes [R, K] and fp32
+    block scales [R, K/32]."""
+    torch = _torch()
+    _cuda_contig(x)
+    R, K = x.shape
+    q = torch.empty((R, K), dtype=torch.int8, device=x.device)
+    d = torch.empty((R, max(K // 32, 1)), dtype=torch.float32, device=x.device)
+    _check(lib().qquantize_act_q8(_p(x), _dtype_code(x), R, K, _p(q), _p(d), _stream()),
+           "qquantize_act_q8")
+    return q, d
+
+
+def gemv_q8_0_i8(W, N, K, q, d, out=None):
+    """y [R, N] = Q8_0 W [N, K] times the int8 activations (q, d)."""
+    torch = _torch()
+    _cuda_contig(W, q, d)
+    R = q.shape[0]
+    if out is None:
+        out = torch.empty((R, N), dtype=torch.float32, device=q.device)
+    _check(lib().qgemv_q8_0_i8(_p(W), N, K, _p(q), _p(d), R, _p(out), _stream()),
+           "qgemv_q8_0_i8")
+    return out
 
 
 def gemm_mxfp4_mxfp8(W, N, K, codes, scales, out=None):

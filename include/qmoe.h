@@ -331,6 +331,22 @@ int qquantize_act_mxfp8(const void *x, int x_dtype, int R, int K,
 int qgemm_mxfp4_mxfp8(const void *W, int N, int K, const uint8_t *codes,
                       const uint8_t *scales, int R, float *y, void *stream);
 
+/* ------------------------------------------- int8 activations, decode ----
+ * Q8_0 weights against int8 activations with integer dot products ([P1]
+ * "NInfer 80 SM port", its int8 artifact and section 八.2: decode quantizes
+ * the activations to int8 and takes dp4a-class dot products).
+ * qquantize_act_q8: x [R, K] (x_dtype) -> q [R, K] int8 and d [R, K/32] fp32:
+ *   per 32 values d = max|x| / 127, q = round-half-away(x / d) clamped to
+ *   [-127, 127] (fp32 divisions, correctly rounded; zero block: d = 0, q = 0).
+ *   K % 32 == 0; x and q 16-byte aligned.
+ * qgemv_q8_0_i8: y [R, N] fp32 = sum_b d_w[n, b] d[r, b] sum_{k in b} q_w q
+ *   (exact int32 per 32-value block, then fp32) for Q8_0 W [N, K] (256-byte
+ *   aligned).  R <= 16, K % 32 == 0.                                        */
+int qquantize_act_q8(const void *x, int x_dtype, int R, int K, int8_t *q,
+                     float *d, void *stream);
+int qgemv_q8_0_i8(const void *W, int N, int K, const int8_t *q, const float *d,
+                  int R, float *y, void *stream);
+
 /* moe_layer_decode: the whole routed-expert layer of a decode step in one
  * launch ([P2] "瓶颈分析": router top-k over the experts, the selected
  * experts' SwiGLU FFNs, their weighted sum; "优化策略二/三": tiers of mixed

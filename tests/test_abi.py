@@ -205,3 +205,12 @@ def test_mx_gemm_validation(L):
     assert L.qgemm_mxfp4_mxfp8(ctypes.c_void_p(256 * 1000 + 16), 16, 128, fake, fake, 4, fake,
                                None) == -1                                    # W alignment
     assert L.qgemm_mxfp4_mxfp8(fake, 0, 128, fake, fake, 4, fake, None) == 0
+
+
+def test_int8_gemv_validation(L):
+    fake = ctypes.c_void_p(256 * 1000)  # never dereferenced: every call below fails validation
+    assert L.qquantize_act_q8(fake, 0, 4, 48, fake, fake, None) == -1      # K % 32
+    assert L.qquantize_act_q8(fake, 3, 4, 64, fake, fake, None) == -2      # dtype
+    assert L.qgemv_q8_0_i8(fake, 16, 64, fake, fake, 17, fake, None) == -1  # R > 16
+    assert L.qgemv_q8_0_i8(fake, 16, 48, fake, fake, 2, fake, None) == -1   # K % 32
+    assert L.qgemv_q8_0_i8(fake, 0, 64, fake, fake, 2, fake, None) == 0
