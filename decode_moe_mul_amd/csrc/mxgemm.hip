@@ -76,79 +76,116 @@ struct MxParams {
   int N, K, R;
 };
 
-struct MxA {  // one lane's A operand of one 16-row group and step
-  uint4 lo, hi;
-  uint32_t s;
-};
-struct MxB {  // one lane's B operand of one 16-column block and step
-  uint4 q;
-  uint32_t s;
-};
+// Block (bx, by): rows by * 128 .., columns bx * 128 ..; wave w computes
+// the 64 x 64 quarter (w >> 1, w & 1): 4 row groups x 4 column blocks, 16
+// matrix ops per K step of 128.  Each step's operand tiles (A: 128 rows x
+// 128 bytes, B: 128 columns x 64 bytes, and their scale words) are loaded
+// once per block with 16-byte coalesced loads into registers while the
+// previous step is multiplied, then written to the other half of a
+// double-buffered LDS tile.  16-byte chunk c of A row r sits at chunk
+// c ^ (r & 7), chunk c of B column n at c ^ (n & 3), so the 16 rows (or
+// columns) one operand read touches spread over the banks.  Rows and columns
+// past the ends re-read the last one (never stored).
+constexpr int kMxAB = kMxBM * 128, kMxBB = kMxBN * 64;  // operand bytes per step
+constexpr size_t kMxLds = 2 * (kMxAB + kMxBB + 4 * (kMxBM + kMxBN));
 
-// Block (bx, by): rows by * 128 .., columns bx * 128 ..; wave w takes the
-// 64 x 64 quarter (w >> 1, w & 1): 4 row groups x 4 column blocks, 16 matrix
-// ops per step against 4 + 4 operand loads.  Loads of step s + 1 are in
-// flight while step s is multiplied.  Rows and columns past the ends re-read
-// the last one (never stored), so every load is unconditional.
-__global__ __launch_bounds__(kMxBlock) void mxfp4_gemm_kernel(MxParams P) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__global__ __launch_bounds__(kMxBlock, 2) void mxfp4_gemm_kernel(MxParams P) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, g = lane >> 4;
   const int K = P.K, nbk = K >> 5, nsteps = K >> 7;
-  const int r0 = blockIdx.y * kMxBM + (wave >> 1) * (16 * kMxMI);
-  const int c0 = blockIdx.x * kMxBN + (wave & 1) * (16 * kMxNB);
-  uint32_t arow[kMxMI], bcol[kMxNB];
+  const int br0 = blockIdx.y * kMxBM, bc0 = blockIdx.x * kMxBN;
+  // LDS: [buf] A bytes, B bytes, A scale words, B scale words
+  auto As = [&](int buf) { return smem + buf * (kMxAB + kMxBB + 4 * (kMxBM + kMxBN)); };
+  auto Bs = [&](int buf) { return As(buf) + kMxAB; };
+  auto Asc = [&](int buf) { return (uint32_t*)(Bs(buf) + kMxBB); };
+  auto Bsc = [&](int buf) { return Asc(buf) + kMxBM; };
+  // staging roles: A chunks tid + 256 j (j < 4): row >> 3, chunk & 7; B chunks
+  // tid + 256 j (j < 2): column >> 2, chunk & 3; thread tid < 128 loads the
+  // scale word of A row tid, the others that of B column tid - 128
+  uint32_t arow_g[4], bcol_g[2];
 #pragma unroll
-  for (int i = 0; i < kMxMI; ++i) arow[i] = (uint32_t)min(r0 + 16 * i + li, P.R - 1);
+  for (int j = 0; j < 4; ++j) arow_g[j] = (uint32_t)min(br0 + ((tid + 256 * j) >> 3), P.R - 1);
 #pragma unroll
-  for (int b = 0; b < kMxNB; ++b) bcol[b] = (uint32_t)min(c0 + 16 * b + li, P.N - 1);
-  auto load = [&](int s, MxA (&a)[kMxMI], MxB (&w)[kMxNB]) {
-    const uint32_t k0 = (uint32_t)s * 128u, blk = (uint32_t)s * 4u + (uint32_t)g;
-#pragma unroll
-    for (int i = 0; i < kMxMI; ++i) {
-      const uint8_t* row = P.xq + arow[i] * (uint32_t)K + k0;
-      a[i].lo = *(const uint4*)(row + 16u * g);
-      a[i].hi = *(const uint4*)(row + 64u + 16u * g);
-      a[i].s = P.xs[arow[i] * (uint32_t)nbk + blk];
-    }
-#pragma unroll
-    for (int b = 0; b < kMxNB; ++b) {
-      w[b].q = *(const uint4*)(P.wq + bcol[b] * (uint32_t)(K >> 1) + 16u * blk);
-      w[b].s = P.ws[bcol[b] * (uint32_t)nbk + blk];
-    }
+  for (int j = 0; j < 2; ++j) bcol_g[j] = (uint32_t)min(bc0 + ((tid + 256 * j) >> 2), P.N - 1);
+  const bool sc_a = tid < kMxBM;
+  const uint32_t sc_row = (uint32_t)(sc_a ? min(br0 + tid, P.R - 1) : min(bc0 + tid - kMxBM, P.N - 1));
+  // one step's operand loads of this thread (named registers: an array here
+  // would be placed in scratch)
+  uint4 va0, va1, va2, va3, vb0, vb1;
+  uint32_t vs;
+  const uint8_t* sp = sc_a ? P.xs : P.ws;
+  auto aptr = [&](int j, uint32_t k0) {
+    return (const uint4*)(P.xq + arow_g[j] * (uint32_t)K + k0 + 16u * ((tid + 256 * j) & 7));
   };
+  auto bptr = [&](int j, uint32_t k0) {
+    return (const uint4*)(P.wq + bcol_g[j] * (uint32_t)(K >> 1) + (k0 >> 1) +
+                          16u * ((tid + 256 * j) & 3));
+  };
+  auto gload = [&](int st) {
+    const uint32_t k0 = (uint32_t)st * 128u;
+    va0 = *aptr(0, k0); va1 = *aptr(1, k0); va2 = *aptr(2, k0); va3 = *aptr(3, k0);
+    vb0 = *bptr(0, k0); vb1 = *bptr(1, k0);
+    vs = *(const uint32_t*)(sp + sc_row * (uint32_t)nbk + 4u * st);
+  };
+  auto awrite = [&](int buf, int j, uint4 v) {
+    const int c = tid + 256 * j, r = c >> 3, ch = c & 7;
+    *(uint4*)(As(buf) + r * 128 + 16 * (ch ^ (r & 7))) = v;
+  };
+  auto bwrite = [&](int buf, int j, uint4 v) {
+    const int c = tid + 256 * j, n = c >> 2, ch = c & 3;
+    *(uint4*)(Bs(buf) + n * 64 + 16 * (ch ^ (n & 3))) = v;
+  };
+  auto lwrite = [&](int buf) {
+    awrite(buf, 0, va0); awrite(buf, 1, va1); awrite(buf, 2, va2); awrite(buf, 3, va3);
+    bwrite(buf, 0, vb0); bwrite(buf, 1, vb1);
+    Asc(buf)[tid] = vs;  // A scale words, then B's (tid - 128) right after
+  };
+  const int wr0 = (wave >> 1) * (16 * kMxMI), wc0 = (wave & 1) * (16 * kMxNB);
   mx_v4f acc[kMxMI][kMxNB];
 #pragma unroll
   for (int i = 0; i < kMxMI; ++i)
 #pragma unroll
     for (int b = 0; b < kMxNB; ++b) acc[i][b] = mx_v4f{0.f, 0.f, 0.f, 0.f};
-  auto mma = [&](const MxA (&a)[kMxMI], const MxB (&w)[kMxNB]) {
+  auto compute = [&](int buf) {
+    uint4 bq[kMxNB];
+    uint32_t bs[kMxNB];
 #pragma unroll
-    for (int i = 0; i < kMxMI; ++i)
+    for (int b = 0; b < kMxNB; ++b) {
+      const int n = wc0 + 16 * b + li;
+      bq[b] = *(const uint4*)(Bs(buf) + n * 64 + 16 * (g ^ (n & 3)));
+      bs[b] = (Bsc(buf)[n] >> (8 * g)) & 0xFFu;
+    }
 #pragma unroll
-      for (int b = 0; b < kMxNB; ++b)
-        acc[i][b] = mx_mma(a[i].lo, a[i].hi, a[i].s, w[b].q, w[b].s, acc[i][b]);
+    for (int i = 0; i < kMxMI; ++i) {
+      const int r = wr0 + 16 * i + li;
+      const uint4 lo = *(const uint4*)(As(buf) + r * 128 + 16 * (g ^ (r & 7)));
+      const uint4 hi = *(const uint4*)(As(buf) + r * 128 + 16 * ((g + 4) ^ (r & 7)));
+      const uint32_t as = (Asc(buf)[r] >> (8 * g)) & 0xFFu;
+#pragma unroll
+      for (int b = 0; b < kMxNB; ++b) acc[i][b] = mx_mma(lo, hi, as, bq[b], bs[b], acc[i][b]);
+    }
   };
-  MxA a0[kMxMI], a1[kMxMI];
-  MxB w0[kMxNB], w1[kMxNB];
-  const int last = nsteps - 1;
-  load(0, a0, w0);
-  int s = 0;
-  for (; s + 1 < nsteps; s += 2) {
-    load(s + 1, a1, w1);
-    mma(a0, w0);
-    load(min(s + 2, last), a0, w0);
-    mma(a1, w1);
+  // the prefetch past the last step re-reads the last step and fills the
+  // buffer nobody reads any more, so the loop has no branches
+  gload(0);
+  lwrite(0);
+  __syncthreads();
+  for (int st = 0; st < nsteps; ++st) {
+    gload(min(st + 1, nsteps - 1));
+    compute(st & 1);
+    lwrite((st + 1) & 1);
+    __syncthreads();
   }
-  if (s < nsteps) mma(a0, w0);
   // lane holds rows 4 g + j of each row group, column li of each block
 #pragma unroll
   for (int i = 0; i < kMxMI; ++i)
 #pragma unroll
     for (int b = 0; b < kMxNB; ++b) {
-      const int col = c0 + 16 * b + li;
+      const int col = bc0 + wc0 + 16 * b + li;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int row = r0 + 16 * i + 4 * g + j;
+        const int row = br0 + wr0 + 16 * i + 4 * g + j;
         if (row < P.R && col < P.N) P.y[(size_t)row * P.N + col] = acc[i][b][j];
       }
     }
@@ -186,13 +223,14 @@ int qgemm_mxfp4_mxfp8(const void* W, int N, int K, const uint8_t* codes, const u
   if (N == 0 || R == 0) return QMOE_OK;
   if (!W || !codes || !scales || !y)
     return fail(QMOE_ERR_INVALID_ARG, "qgemm_mxfp4_mxfp8: null pointer");
-  if (!QMOE_ALIGNED(W, 256) || !QMOE_ALIGNED(codes, 16))
-    return fail(QMOE_ERR_INVALID_ARG, "qgemm_mxfp4_mxfp8: misaligned W/codes");
+  if (!QMOE_ALIGNED(W, 256) || !QMOE_ALIGNED(codes, 16) || !QMOE_ALIGNED(scales, 4))
+    return fail(QMOE_ERR_INVALID_ARG, "qgemm_mxfp4_mxfp8: misaligned W/codes/scales");
   const Layout L = layout_of(QMOE_MXFP4, N, K);
   MxParams P{(const uint8_t*)W + L.off[0], (const uint8_t*)W + L.off[1], codes, scales, y, N, K, R};
   const dim3 grid((unsigned)((N + kMxBN - 1) / kMxBN), (unsigned)((R + kMxBM - 1) / kMxBM));
   if (grid.y > 65535) return fail(QMOE_ERR_UNSUPPORTED, "qgemm_mxfp4_mxfp8: R=%d too large", R);
-  return QMOE_LAUNCH("mxfp4_gemm", mxfp4_gemm_kernel, grid, kMxBlock, 0, (hipStream_t)stream, P);
+  return QMOE_LAUNCH("mxfp4_gemm", mxfp4_gemm_kernel, grid, kMxBlock, kMxLds, (hipStream_t)stream,
+                     P);
 }
 
 }  // extern "C"

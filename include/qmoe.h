@@ -325,7 +325,8 @@ int moe_combine(const float *o, const int32_t *inv_perm, const float *p, int T,
  * qgemm_mxfp4_mxfp8: y [R, N] fp32 = sum_k w[n, k] * xq[r, k] for MXFP4
  * weights W [N, K] (qmoe layout, 256-byte aligned) and MXFP8 activations as
  * qquantize_act_mxfp8 writes them; every product is exact, sums are fp32 in
- * the matrix cores.  K % 128 == 0; N*K and R*K < 2^32.                     */
+ * the matrix cores.  K % 128 == 0; N*K and R*K < 2^32; codes 16-byte and
+ * scales 4-byte aligned.                                                    */
 int qquantize_act_mxfp8(const void *x, int x_dtype, int R, int K,
                         uint8_t *codes, uint8_t *scales, void *stream);
 int qgemm_mxfp4_mxfp8(const void *W, int N, int K, const uint8_t *codes,
