@@ -110,10 +110,9 @@ __global__ __launch_bounds__(kMxBlock, 2) void mxfp4_gemm_kernel(MxParams P) {
   for (int j = 0; j < 2; ++j) bcol_g[j] = (uint32_t)min(bc0 + ((tid + 256 * j) >> 2), P.N - 1);
   const bool sc_a = tid < kMxBM;
   const uint32_t sc_row = (uint32_t)(sc_a ? min(br0 + tid, P.R - 1) : min(bc0 + tid - kMxBM, P.N - 1));
-  // one step's operand loads of this thread (named registers: an array here
-  // would be placed in scratch)
-  uint4 va0, va1, va2, va3, vb0, vb1;
-  uint32_t vs;
+  // two steps of this thread's operand loads in flight, in sets X and Y
+  // (named registers: an array here would be placed in scratch)
+  struct Set { uint4 a0, a1, a2, a3, b0, b1; uint32_t s; };
   const uint8_t* sp = sc_a ? P.xs : P.ws;
   auto aptr = [&](int j, uint32_t k0) {
     return (const uint4*)(P.xq + arow_g[j] * (uint32_t)K + k0 + 16u * ((tid + 256 * j) & 7));
@@ -122,11 +121,11 @@ __global__ __launch_bounds__(kMxBlock, 2) void mxfp4_gemm_kernel(MxParams P) {
     return (const uint4*)(P.wq + bcol_g[j] * (uint32_t)(K >> 1) + (k0 >> 1) +
                           16u * ((tid + 256 * j) & 3));
   };
-  auto gload = [&](int st) {
+  auto gload = [&](int st, Set& v) {
     const uint32_t k0 = (uint32_t)st * 128u;
-    va0 = *aptr(0, k0); va1 = *aptr(1, k0); va2 = *aptr(2, k0); va3 = *aptr(3, k0);
-    vb0 = *bptr(0, k0); vb1 = *bptr(1, k0);
-    vs = *(const uint32_t*)(sp + sc_row * (uint32_t)nbk + 4u * st);
+    v.a0 = *aptr(0, k0); v.a1 = *aptr(1, k0); v.a2 = *aptr(2, k0); v.a3 = *aptr(3, k0);
+    v.b0 = *bptr(0, k0); v.b1 = *bptr(1, k0);
+    v.s = *(const uint32_t*)(sp + sc_row * (uint32_t)nbk + 4u * st);
   };
   auto awrite = [&](int buf, int j, uint4 v) {
     const int c = tid + 256 * j, r = c >> 3, ch = c & 7;
@@ -136,10 +135,10 @@ __global__ __launch_bounds__(kMxBlock, 2) void mxfp4_gemm_kernel(MxParams P) {
     const int c = tid + 256 * j, n = c >> 2, ch = c & 3;
     *(uint4*)(Bs(buf) + n * 64 + 16 * (ch ^ (n & 3))) = v;
   };
-  auto lwrite = [&](int buf) {
-    awrite(buf, 0, va0); awrite(buf, 1, va1); awrite(buf, 2, va2); awrite(buf, 3, va3);
-    bwrite(buf, 0, vb0); bwrite(buf, 1, vb1);
-    Asc(buf)[tid] = vs;  // A scale words, then B's (tid - 128) right after
+  auto lwrite = [&](int buf, const Set& v) {
+    awrite(buf, 0, v.a0); awrite(buf, 1, v.a1); awrite(buf, 2, v.a2); awrite(buf, 3, v.a3);
+    bwrite(buf, 0, v.b0); bwrite(buf, 1, v.b1);
+    Asc(buf)[tid] = v.s;  // A scale words, then B's (tid - 128) right after
   };
   const int wr0 = (wave >> 1) * (16 * kMxMI), wc0 = (wave & 1) * (16 * kMxNB);
   mx_v4f acc[kMxMI][kMxNB];
@@ -166,17 +165,28 @@ __global__ __launch_bounds__(kMxBlock, 2) void mxfp4_gemm_kernel(MxParams P) {
       for (int b = 0; b < kMxNB; ++b) acc[i][b] = mx_mma(lo, hi, as, bq[b], bs[b], acc[i][b]);
     }
   };
-  // the prefetch past the last step re-reads the last step and fills the
-  // buffer nobody reads any more, so the loop has no branches
-  gload(0);
-  lwrite(0);
+  // LDS buffer s & 1 holds step s; set X holds the next odd step, Y the
+  // next even one.  Prefetches past the last step re-read it and fill a
+  // buffer nobody reads any more, so the loop body has no branches.
+  const int last = nsteps - 1;
+  Set X, Y;
+  gload(0, X);
+  lwrite(0, X);
   __syncthreads();
-  for (int st = 0; st < nsteps; ++st) {
-    gload(min(st + 1, nsteps - 1));
-    compute(st & 1);
-    lwrite((st + 1) & 1);
+  gload(min(1, last), X);
+  gload(min(2, last), Y);
+  int st = 0;
+  for (; st + 2 <= nsteps; st += 2) {
+    compute(0);
+    lwrite(1, X);
     __syncthreads();
+    gload(min(st + 3, last), X);
+    compute(1);
+    lwrite(0, Y);
+    __syncthreads();
+    gload(min(st + 4, last), Y);
   }
+  if (st < nsteps) compute(0);  // odd step count: the last step is in buffer 0
   // lane holds rows 4 g + j of each row group, column li of each block
 #pragma unroll
   for (int i = 0; i < kMxMI; ++i)
