@@ -71,6 +71,8 @@ __global__ __launch_bounds__(256) void quantize_act_q8_kernel(const void* x, int
 }
 
 // ----------------------------------------------------------- the GEMV ----
+constexpr int kI8Batch = 4;  // units per lane whose loads are in flight together
+
 struct I8Params {
   const int8_t* wq;       // [N][K]
   const uint16_t* wd;     // [N][K/32] fp16
@@ -107,22 +109,39 @@ __global__ __launch_bounds__(256) void qgemv_q8_0_i8_kernel(I8Params P) {
       float acc[RC];
 #pragma unroll
       for (int r = 0; r < RC; ++r) acc[r] = 0.f;
-      for (int u = g; u < U; u += G) {
-        const uint4 w0 = *(const uint4*)(wr + 32 * u), w1 = *(const uint4*)(wr + 32 * u + 16);
-        const float dw = f16_bits_to_f32(wdr[u]);
-        const int wv[8] = {(int)w0.x, (int)w0.y, (int)w0.z, (int)w0.w,
-                           (int)w1.x, (int)w1.y, (int)w1.z, (int)w1.w};
+      // the lane's units g, g + G, ... in batches of kI8Batch whose loads are
+      // all issued before the first is used (a batch past the lane's last
+      // unit re-reads that unit and adds nothing)
+      const int nu = U / G;
+      for (int i0 = 0; i0 < nu; i0 += kI8Batch) {
+        uint4 w0[kI8Batch], w1[kI8Batch];
+        uint16_t sc[kI8Batch];
 #pragma unroll
-        for (int r = 0; r < RC; ++r) {
-          if (r < rc) {
-            const uint4 a0 = *(const uint4*)(xs + (size_t)r * K + 32 * u);
-            const uint4 a1 = *(const uint4*)(xs + (size_t)r * K + 32 * u + 16);
-            const int av[8] = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
-                               (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-            int s = 0;
+        for (int j = 0; j < kI8Batch; ++j) {
+          const int u = g + G * min(i0 + j, nu - 1);
+          w0[j] = load_stream((const uint4*)(wr + 32 * u));
+          w1[j] = load_stream((const uint4*)(wr + 32 * u + 16));
+          sc[j] = wdr[u];
+        }
 #pragma unroll
-            for (int j = 0; j < 8; ++j) s = __builtin_amdgcn_sdot4(wv[j], av[j], s, false);
-            acc[r] = fmaf((float)s, dw * xds[r * U + u], acc[r]);
+        for (int j = 0; j < kI8Batch; ++j) {
+          if (i0 + j >= nu) break;
+          const int u = g + G * (i0 + j);
+          const float dw = f16_bits_to_f32(sc[j]);
+          const int wv[8] = {(int)w0[j].x, (int)w0[j].y, (int)w0[j].z, (int)w0[j].w,
+                             (int)w1[j].x, (int)w1[j].y, (int)w1[j].z, (int)w1[j].w};
+#pragma unroll
+          for (int r = 0; r < RC; ++r) {
+            if (r < rc) {
+              const uint4 a0 = *(const uint4*)(xs + (size_t)r * K + 32 * u);
+              const uint4 a1 = *(const uint4*)(xs + (size_t)r * K + 32 * u + 16);
+              const int av[8] = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
+                                 (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+              int s = 0;
+#pragma unroll
+              for (int q = 0; q < 8; ++q) s = __builtin_amdgcn_sdot4(wv[q], av[q], s, false);
+              acc[r] = fmaf((float)s, dw * xds[r * U + u], acc[r]);
+            }
           }
         }
       }
