@@ -156,18 +156,21 @@ int t5_check(const char* who, const qmoe_gemv_desc& q);             // ternary.h
 int t5_batch_launch(const qmoe_gemv_desc* d, int n, void* stream);  // ternary.hip
 
 // Rows per block for a dense matrix of mat_bytes in a launch that streams
-// total_bytes: about eight blocks per compute unit overall, but no fewer than
+// total_bytes: per_cu blocks per compute unit overall, but no fewer than
 // kMinBlockBytes of weights per block, since every block stages its own copy
 // of the activation rows; each matrix gets blocks in proportion to its bytes.
 // A multiple of a wave pass and of the 16-row matrix-core blocks.
 constexpr size_t kMinBlockBytes = 64 << 10;
-static int pick_tile_rows_bytes(int N, int G, size_t mat_bytes, size_t total_bytes) {
+constexpr size_t kLdsPerCu = 160 << 10;  // LDS of one CDNA4 compute unit
+static int pick_tile_rows_bytes(int N, int G, size_t mat_bytes, size_t total_bytes,
+                                int per_cu = 8) {
   int group = kWaves * (64 / G);
   if (group < 16) group = 16;
   int cus = cu_count();
   if (cus <= 0) cus = 256;
   const long long by_bytes = (long long)(total_bytes / kMinBlockBytes);
-  const long long blocks = std::min<long long>(8LL * cus, std::max<long long>(cus, by_bytes));
+  const long long blocks =
+      std::min<long long>((long long)per_cu * cus, std::max<long long>(cus, by_bytes));
   long long tiles = total_bytes ? (long long)((double)blocks * mat_bytes / total_bytes) : 1;
   const long long max_tiles = (N + group - 1) / group;
   tiles = std::max<long long>(1, std::min(tiles, max_tiles));
@@ -261,11 +264,22 @@ static int qgemv_batch_launch(const qmoe_gemv_desc* d, int n, void* stream) {
   size_t lds = 0, total_bytes = 0;
   for (int i = 0; i < n; ++i)
     if (d[i].N > 0 && d[i].R > 0) total_bytes += layout_of(d[i].fmt, d[i].N, d[i].K).total;
+  // One round of blocks: as many per compute unit as the largest staging
+  // lets its 160 KB of LDS hold at once, at most eight (a second round of
+  // blocks would start behind a ragged first one).
+  size_t lds_max = 0;
+  for (int i = 0; i < n; ++i)
+    if (d[i].N > 0 && d[i].R > 0)
+      lds_max = std::max(lds_max, d[i].R > pick_rc(d[i].R, d[i].K)
+                                      ? mfma_red_bytes(1)
+                                      : stage_bytes(pick_rc(d[i].R, d[i].K), d[i].K));
+  const int per_cu = lds_max ? (int)std::max<size_t>(1, std::min<size_t>(8, kLdsPerCu / lds_max)) : 8;
   for (int i = 0; i < n; ++i) {
     const qmoe_gemv_desc& q = d[i];
     const int rc = pick_rc(q.R, q.K);
     P.G[i] = lanes_per_row(q.K);
-    int tr = pick_tile_rows_bytes(q.N, P.G[i], layout_of(q.fmt, q.N, q.K).total, total_bytes);
+    int tr = pick_tile_rows_bytes(q.N, P.G[i], layout_of(q.fmt, q.N, q.K).total, total_bytes,
+                                  per_cu);
     const bool mc = q.R > rc;
     P.rc[i] = mc ? 0 : rc;
     any_mfma |= mc;
