@@ -869,15 +869,15 @@ inline int pick_rc(int rows, int K, size_t budget = kLdsCap) {
 }
 
 // Rows per block for N rows when `work_items` independent matrices run in
-// the same launch: about eight blocks per compute unit overall, so that every
+// the same launch: about per_cu blocks per compute unit overall, so that every
 // CU keeps enough weight loads in flight to cover HBM latency.  A multiple of
 // a wave pass and of the 16-row matrix-core blocks.
-inline int pick_tile_rows(int N, int G, int work_items) {
+inline int pick_tile_rows(int N, int G, int work_items, int per_cu = 8) {
   int group = kWaves * (64 / G);
   if (group < 16) group = 16;
   int cus = cu_count();
   if (cus <= 0) cus = 256;
-  const long long want = 8LL * cus;
+  const long long want = (long long)per_cu * cus;
   long long tiles = (want + work_items - 1) / work_items;
   const long long max_tiles = (N + group - 1) / group;
   if (tiles > max_tiles) tiles = max_tiles;

@@ -27,6 +27,7 @@
 //  * Gate and up rows of the same output are handled by the same lanes, so
 //    SiLU(g) * u is applied in registers before anything is stored.
 #include <algorithm>
+#include <cmath>
 #include <cstdio>
 
 #include "decode.hpp"
@@ -360,6 +361,27 @@ size_t moe_ffn_workspace_size(int T, int k, int F) {
   return round_up256((size_t)T * k * F * sizeof(float)) + 256;
 }
 
+// Blocks per CU for one phase of the routed FFN: 8, or more (up to 24) when
+// ranks experts of the phase's largest tier would give blocks of more than
+// 256 KB of weights at 8 per CU.  Long blocks leave a long tail once the
+// last ones start (16 rows through 256 experts of [2048, 7168] Q4_K, about
+// 1 MB per block at 8 per CU; 8 / 12 / 16 / 24 / 32 / 48 per CU: gate/up
+// 376 / 367 / 365 / 354 / 355 / 367 us per step of the three decode calls).
+static int ffn_blocks_per_cu(const qmoe_tier* tiers, int n_tiers, int H, int F, int phase,
+                             int ranks) {
+  size_t worst = 0;
+  for (int i = 0; i < n_tiers; ++i) {
+    const size_t b = phase == 0 ? 2 * layout_of(tiers[i].fmt_gate_up, F, H).total
+                                : layout_of(tiers[i].fmt_down, H, F).total;
+    worst = std::max(worst, b);
+  }
+  int cus = cu_count();
+  if (cus <= 0) cus = 256;
+  const double per_block = (double)ranks * (double)worst / (8.0 * cus);
+  const int steps = (int)std::ceil(per_block / (double)(256 << 10));
+  return std::min(24, std::max(8, 8 * steps));
+}
+
 int moe_ffn_tiered(const qmoe_tier* tiers, int n_tiers, int E, int H, int F, const void* x,
                    int x_dtype, int T, int k, const int32_t* offsets, const int32_t* perm,
                    float* o, void* ws, size_t ws_bytes, void* stream) {
@@ -397,7 +419,8 @@ int moe_ffn_tiered(const qmoe_tier* tiers, int n_tiers, int E, int H, int F, con
   for (int phase = 0; phase < 2; ++phase) {
     const int N = phase == 0 ? F : H, K = phase == 0 ? H : F, rc = phase == 0 ? rc1 : rc2;
     P.G = lanes_per_row(K);
-    P.tile_rows = pick_tile_rows(N, P.G, ranks);
+    P.tile_rows =
+        pick_tile_rows(N, P.G, ranks, ffn_blocks_per_cu(tiers, n_tiers, H, F, phase, ranks));
     P.ntiles = (N + P.tile_rows - 1) / P.tile_rows;
     P.m_max = rc == 0 ? 0 : T > rc ? rc : 0x7FFFFFFF;
     // A many-row expert gets up to (m_max + 1) * ntiles blocks and holds at
