@@ -181,6 +181,54 @@ def _per_dispatch(rows, counter, pick):
     return vals
 
 
+def summarize_trace(trace_dir):
+    """Markdown table of a rocprofv3 --kernel-trace run: per kernel (short
+    name, the routed FFN's phases told apart) and grid size in workgroups,
+    the launch count and the average / min / max duration; then the routed
+    FFN phases' averages over all their launches."""
+    import collections
+    import csv
+    import glob
+    import re
+    path = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)[0]
+
+    def short(name):
+        name = re.sub(r"^void ", "", name).replace("qmoe::", "")
+        m = re.match(r"(\w+)(<[^>]*>)?", name)
+        base = m.group(1) + (m.group(2) or "")
+        if base.startswith("ffn_decode_kernel<0"):
+            return "ffn_gate_up " + base
+        if base.startswith("ffn_decode_kernel<1"):
+            return "ffn_down " + base
+        return base
+
+    by = collections.defaultdict(list)
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            blocks = 1
+            for ax in "XYZ":
+                g = int(r.get(f"Grid_Size_{ax}", "1") or 1)
+                w = int(r.get(f"Workgroup_Size_{ax}", "1") or 1)
+                blocks *= max(1, g // max(1, w))
+            us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            by[(short(r["Kernel_Name"]), blocks)].append(us)
+    keep = ("ffn_", "route", "router", "topk", "permute", "combine", "prefill", "qgemv",
+            "layer", "mxfp4", "quantize_act", "q8_0_i8")
+    print("| kernel | blocks | launches | avg us | min us | max us |")
+    print("|---|---:|---:|---:|---:|---:|")
+    phase = collections.defaultdict(list)
+    for (k, b), v in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+        if not any(k.startswith(p) or p in k for p in keep):
+            continue
+        print(f"| {k} | {b} | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
+        phase[k.split()[0]].extend(v)
+    print()
+    for k in ("ffn_gate_up", "ffn_down"):
+        if phase.get(k):
+            v = phase[k]
+            print(f"{k}: {len(v)} launches, average {sum(v) / len(v):.3f} us")
+
+
 def summarize_pmc(fetch_dir, write_dir):
     """Write TRAFFIC_FILE from the two counter runs."""
     is_gu = lambda r: "ffn_decode_kernel<0" in r["Kernel_Name"]
@@ -436,11 +484,16 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-only", action="store_true",
                     help="skip the dense-GEMV and prefill sections (counter runs)")
+    ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
+                    help="print the per-kernel table of a rocprofv3 --kernel-trace run and exit")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the traffic summary from two rocprofv3 --pmc runs and exit")
     a = ap.parse_args()
     if a.summarize_pmc:
         summarize_pmc(*a.summarize_pmc)
+        return
+    if a.summarize_trace:
+        summarize_trace(a.summarize_trace)
         return
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; the decode path has "
