@@ -361,12 +361,14 @@ size_t moe_ffn_workspace_size(int T, int k, int F) {
   return round_up256((size_t)T * k * F * sizeof(float)) + 256;
 }
 
-// Blocks per CU for one phase of the routed FFN: 8, or more (up to 24) when
-// ranks experts of the phase's largest tier would give blocks of more than
-// 256 KB of weights at 8 per CU.  Long blocks leave a long tail once the
-// last ones start (16 rows through 256 experts of [2048, 7168] Q4_K, about
-// 1 MB per block at 8 per CU; 8 / 12 / 16 / 24 / 32 / 48 per CU: gate/up
-// 376 / 367 / 365 / 354 / 355 / 367 us per step of the three decode calls).
+// Blocks per CU for one phase of the routed FFN: 8 per 256 KB of weights a
+// block would stream at 8 per CU (ranks experts of the phase's largest tier),
+// between 4 and 24.  Long blocks leave a long tail once the last ones start
+// (16 rows through 256 experts of [2048, 7168] Q4_K, about 2 MB per block at
+// 8 per CU; 8 / 12 / 16 / 24 / 32 / 48 per CU: gate/up 376 / 367 / 365 / 354
+// / 355 / 367 us per step of the three decode calls); a few rows through
+// small experts (about 60 KB per block at 8) run faster as fewer, longer
+// blocks (the 6-row tiered call 79.4 -> 75.1 us at 4 per CU).
 static int ffn_blocks_per_cu(const qmoe_tier* tiers, int n_tiers, int H, int F, int phase,
                              int ranks) {
   size_t worst = 0;
@@ -378,8 +380,7 @@ static int ffn_blocks_per_cu(const qmoe_tier* tiers, int n_tiers, int H, int F, 
   int cus = cu_count();
   if (cus <= 0) cus = 256;
   const double per_block = (double)ranks * (double)worst / (8.0 * cus);
-  const int steps = (int)std::ceil(per_block / (double)(256 << 10));
-  return std::min(24, std::max(8, 8 * steps));
+  return std::min(24, std::max(4, (int)(8.0 * per_block / (double)(256 << 10))));
 }
 
 int moe_ffn_tiered(const qmoe_tier* tiers, int n_tiers, int E, int H, int F, const void* x,
