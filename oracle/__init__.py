@@ -21,6 +21,13 @@ path computes, in float64 NumPy:
   cross-check the vectorised oracle.
 
 Parity status: every public function is pinned by a CPU test in
-``tests/test_oracle_*.py`` (closed-form blocks, error bounds, brute force,
-invariants).  No function is "parity unpinned".
+``tests/test_oracle_*.py`` against something other than the oracle itself:
+closed-form blocks and quantizer error bounds (``formats``, ``mx``,
+``int8``), scalar loops over the packed bytes and exhaustive code searches
+(``brute``, the MX expert FFN, the int8 GEMV), enumeration of every k-subset
+(``topk`` and the selection margin ``topk_gap``), NumPy's stable argsort
+(``permute``) and layer invariants (top-1 routing equals the dense FFN, token
+reordering, shared-only routing).  The helpers ``router_logits``,
+``softmax_over`` and ``silu`` are pinned through ``route`` and the brute-force
+layers that call them.
 """

@@ -217,8 +217,3 @@ def moe_layer(x, ids, p, get_expert, H, F, E):
             y[t] += p[t, i] * r["o"][j]
             b[t] += p[t, i] * r["bound_o"][j]
     return y, b
-
-
-def experts_touched(ids, E):
-    flat = np.asarray(ids).reshape(-1)
-    return np.unique(flat[(flat >= 0) & (flat < E)])

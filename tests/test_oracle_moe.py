@@ -9,6 +9,8 @@ Checked against things other than the oracle itself:
     reordering tokens reorders outputs, shared-only routing returns the
     shared expert, bounds dominate values.
 """
+import math
+
 import numpy as np
 import pytest
 
@@ -105,6 +107,69 @@ def test_topk_ties_and_nan():
     assert list(moe.topk(np.full((1, 4), np.nan), 2)[0]) == [0, 1]
     with np.errstate(invalid="ignore"):
         assert list(moe.topk(np.array([[-np.inf, np.nan, -1.0]]), 2)[0]) == [2, 0]
+
+
+def test_router_logits_scalar_loops():
+    """logits[t, e] = sum_h x[t, h] Wr[e, h] + b[e], summed by hand."""
+    x = synth.normal((3, 40), 1.0, 5, synth.ACT)
+    Wr = synth.normal((7, 40), 0.02, 5, synth.ROUTER)
+    b = synth.rank_prior(7, 0.5)
+    got = moe.router_logits(x, Wr, b)
+    for t in range(3):
+        for e in range(7):
+            want = sum(float(x[t, h]) * float(Wr[e, h]) for h in range(40)) + float(b[e])
+            assert got[t, e] == pytest.approx(want, rel=1e-12, abs=1e-14)
+    assert np.array_equal(moe.router_logits(x, Wr), moe.router_logits(x, Wr, np.zeros(7)))
+
+
+def test_topk_gap_is_the_selection_margin():
+    """topk_gap = (smallest kept logit) - (largest dropped logit), with the kept
+    set taken from the k-subset enumeration; 0 on a tie across the cut, inf
+    when every expert is kept."""
+    rng = np.random.default_rng(7)
+    for trial in range(60):
+        E = int(rng.integers(2, 9))
+        k = int(rng.integers(1, E + 1))
+        T = 3
+        logits = rng.standard_normal((T, E)).round(1)      # rounding makes ties
+        gap = moe.topk_gap(logits, k)
+        for t in range(T):
+            row = [float(v) for v in logits[t]]
+            kept = brute.topk_by_enumeration(row, k)
+            dropped = [e for e in range(E) if e not in kept]
+            want = (min(row[e] for e in kept) - max(row[e] for e in dropped)
+                    if dropped else math.inf)
+            assert gap[t] == want, (row, k)
+            assert gap[t] >= 0
+    assert moe.topk_gap(np.array([[1.0, 2.0, 2.0, 0.5]]), 1)[0] == 0.0   # tie at the cut
+    assert moe.topk_gap(np.array([[1.0, 2.0, 2.0, 0.5]]), 2)[0] == 1.0
+    assert moe.topk_gap(np.array([[1.0, 2.0, 3.0]]), 3)[0] == math.inf
+
+
+def test_topk_gap_bounds_the_perturbation_that_keeps_the_selection():
+    """The property the GPU routing tests rely on: perturbing every logit by
+    less than gap / 2 cannot change the kept set (the near-tie protocol
+    compares ids only for tokens whose gap exceeds twice the logit error)."""
+    rng = np.random.default_rng(8)
+    T, E, k = 200, 64, 6
+    logits = rng.standard_normal((T, E))
+    gap = moe.topk_gap(logits, k)
+    base = moe.topk(logits, k)
+    for t in range(T):
+        err = 0.499 * gap[t]
+        for _ in range(5):
+            pert = logits[t] + rng.uniform(-err, err, E)
+            got = moe.topk(pert[None, :], k)[0]
+            assert set(got.tolist()) == set(base[t].tolist())
+    # and a perturbation of just over gap / 2 at the two logits across the
+    # cut swaps them
+    t = 0
+    srt = np.argsort(-logits[t], kind="stable")
+    pert = logits[t].copy()
+    pert[srt[k - 1]] -= 0.51 * gap[t]
+    pert[srt[k]] += 0.51 * gap[t]
+    got = moe.topk(pert[None, :], k)[0]
+    assert srt[k] in got and srt[k - 1] not in got
 
 
 def test_route_weights():

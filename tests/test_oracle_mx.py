@@ -122,3 +122,68 @@ def test_mx_gemm_against_brute_force():
             acc_abs += abs(wv * xv)
         assert y[r, n] == pytest.approx(acc, rel=1e-12, abs=1e-15)
         assert bound[r, n] == pytest.approx(acc_abs, rel=1e-12)
+
+
+def _e4m3_scalar(c):
+    """E4M3 value from its bit fields (OCP MX v1.0), finite codes only."""
+    s = -1.0 if c & 0x80 else 1.0
+    e, m = (c >> 3) & 15, c & 7
+    return s * (math.ldexp(m / 8.0, -6) if e == 0 else math.ldexp(1.0 + m / 8.0, e - 7))
+
+
+_POS = [_e4m3_scalar(c) for c in range(0x7F)]
+
+
+def _mxfp8_scalar(block):
+    """One 32-value block quantized and dequantized element by element: the
+    shared exponent from the largest magnitude, every element to the nearest
+    of the 127 non-negative E4M3 values by search (ties to the even code,
+    saturating at 448)."""
+    amax = max(abs(v) for v in block)
+    if amax == 0:
+        return [0.0] * len(block)
+    e = min(max(math.frexp(amax)[1] - 1 - 8 + 127, 0), 254)
+    scale = math.ldexp(1.0, e - 127)
+    out = []
+    for v in block:
+        m = abs(v) / scale
+        best, bd = 0, None
+        for c, g in enumerate(_POS):
+            d = abs(g - m)
+            if bd is None or d < bd or (d == bd and c % 2 == 0):
+                best, bd = c, d
+        out.append(math.copysign(_POS[best] * scale, v) if best else 0.0)
+    return out
+
+
+def test_mx_expert_ffn_against_scalar_brute_force():
+    """One MXFP4/MXFP4 expert on the block-scaled path, element by element:
+    x quantized to MXFP8 per 32 values along H, g and u from the packed gate
+    and up bytes, h = SiLU(g) u quantized per 32 values along F (the down
+    projection's reduction axis), o from the packed down bytes.  Two rows and
+    F = 96 (three blocks along F) so that quantizing along the wrong axis or
+    over the wrong span changes the result."""
+    rng = np.random.default_rng(11)
+    H, F, R = 64, 96, 2
+    gbuf = fm.quantize("mxfp4", rng.normal(0, 0.2, (F, H)))
+    ubuf = fm.quantize("mxfp4", rng.normal(0, 0.2, (F, H)))
+    dbuf = fm.quantize("mxfp4", rng.normal(0, 0.2, (H, F)))
+    X = rng.normal(0, 1, (R, H)) * np.array([[1.0], [37.0]])
+    o, bound = mx.mx_expert_ffn(gbuf, ubuf, dbuf, H, F, X)
+    assert o.shape == (R, H) and bound.shape == (R, H)
+    for r in range(R):
+        xq = []
+        for b in range(H // 32):
+            xq += _mxfp8_scalar([float(v) for v in X[r, 32 * b:32 * b + 32]])
+        g = [sum(brute.element("mxfp4", gbuf, F, H, n, k) * xq[k] for k in range(H))
+             for n in range(F)]
+        u = [sum(brute.element("mxfp4", ubuf, F, H, n, k) * xq[k] for k in range(H))
+             for n in range(F)]
+        h = [gi / (1.0 + math.exp(-gi)) * ui for gi, ui in zip(g, u)]
+        hq = []
+        for b in range(F // 32):
+            hq += _mxfp8_scalar(h[32 * b:32 * b + 32])
+        for n in range(H):
+            terms = [brute.element("mxfp4", dbuf, H, F, n, j) * hq[j] for j in range(F)]
+            assert o[r, n] == pytest.approx(sum(terms), rel=1e-12, abs=1e-14)
+            assert bound[r, n] == pytest.approx(sum(abs(t) for t in terms), rel=1e-12)
