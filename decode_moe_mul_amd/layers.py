@@ -122,6 +122,11 @@ class MoELayer:
             self._ws[key] = ws
         return self._ws[key]
 
+    def check_one_launch(self, T):
+        """Raise if a one-launch call with T rows reported a barrier time-out
+        since the last check (the workspace's sticky error word)."""
+        qmoe.check_layer_decode(self.workspaces(T)["layer"])
+
     def _fused(self, T, prefill):
         """Decode rows route and permute in one launch (moe_route_decode)."""
         c = self.cfg
@@ -129,13 +134,15 @@ class MoELayer:
         return (not prefill and T <= 16 and c.E <= 512
                 and ((T * kt + 63) // 64) * 64 + 16 + c.E_total <= 8192)
 
-    def forward(self, x, copy=0, prefill=False, one_launch=False, mx=False):
+    def forward(self, x, copy=0, prefill=False, one_launch=False, mx=False, check=True):
         """y [T, H] for activations x [T, H] (float32 or bfloat16).  The
         intermediate ids, p, offsets, perm, inv (and o, unless one_launch)
         stay in the workspace dict returned second.  one_launch: the whole
-        decode layer as moe_layer_decode (T <= 16).  mx (with prefill): the
-        MXFP4/MXFP4 tiers on the block-scaled matrix cores
-        (qgemm_grouped_prefill_mx)."""
+        decode layer as moe_layer_decode (T <= 16); with check (the default)
+        the call is waited for and its barrier error word read (a timing
+        loop passes check=False and calls check_one_launch(T) afterwards).
+        mx (with prefill): the MXFP4/MXFP4 tiers on the block-scaled matrix
+        cores (qgemm_grouped_prefill_mx)."""
         c = self.cfg
         T = x.shape[0]
         ws = self.workspaces(T, prefill)
@@ -150,6 +157,8 @@ class MoELayer:
                 qmoe._p(ws["p"]), qmoe._p(ws["offsets"]), qmoe._p(ws["perm"]),
                 qmoe._p(ws["inv"]), qmoe._p(ws["y"]), qmoe._p(ws["layer"]), ws["layer"].numel(),
                 s), "moe_layer_decode")
+            if check:
+                qmoe.check_layer_decode(ws["layer"])
             return ws["y"], ws
         if self._fused(T, prefill):
             qmoe._check(L.moe_route_decode(

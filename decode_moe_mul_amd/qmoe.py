@@ -70,6 +70,7 @@ _SIGNATURES = {
     "moe_layer_decode_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "moe_layer_decode": (_I, [ctypes.POINTER(Tier), _I, _I, _I, _I, _VP, _I, _I, _VP, _VP, _I,
                               _I, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
+    "qmoe_stream_read": (_I, [_VP, _SZ, _I, _VP, _VP]),
     "qmoe_profile_enable": (_I, [_I]),
     "qmoe_profile_reset": (_I, []),
     "qmoe_profile_only": (_I, [ctypes.c_char_p]),
@@ -420,9 +421,30 @@ def layer_decode_workspace(T, H, E, F, k, n_shared=0, device="cuda"):
     return torch.zeros(max(int(n), 1), dtype=torch.uint8, device=device)
 
 
-def layer_decode(tiers, E, H, F, x, Wr, bias, k, n_shared=0, out=None, ws=None):
+def layer_decode_error(ws):
+    """The error word of a moe_layer_decode workspace (waits for the stream):
+    nonzero once a grid-barrier wait of some call on it ran out, which makes
+    that call's outputs invalid.  The word stays set until cleared."""
+    torch = _torch()
+    torch.cuda.current_stream().synchronize()
+    return int(ws[:4].view(torch.int32).item())
+
+
+def check_layer_decode(ws):
+    """Raise QmoeError if the workspace's error word is set (clearing it, so
+    that the workspace can be used again)."""
+    if layer_decode_error(ws):
+        ws[:4].zero_()
+        raise QmoeError("moe_layer_decode: a grid-barrier wait ran out; the outputs of the "
+                        "calls since the workspace was last checked are invalid")
+
+
+def layer_decode(tiers, E, H, F, x, Wr, bias, k, n_shared=0, out=None, ws=None, check=True):
     """The whole routed-expert layer for decode rows (T <= 16) in one launch:
-    y [T, H] and the routing ids, p, offsets, perm, inv_perm."""
+    y [T, H] and the routing ids, p, offsets, perm, inv_perm.  check: wait
+    for the call and raise if its barrier error word is set (callers that
+    queue many calls may pass False and call check_layer_decode(ws) once
+    afterwards: the word is sticky)."""
     torch = _torch()
     _cuda_contig(x, Wr, bias)
     T = x.shape[0]
@@ -442,7 +464,23 @@ def layer_decode(tiers, E, H, F, x, Wr, bias, k, n_shared=0, out=None, ws=None):
                                   _p(bias), k, n_shared, _p(ids), _p(p), _p(offsets), _p(perm),
                                   _p(inv), _p(out), _p(ws), ws.numel(), _stream()),
            "moe_layer_decode")
+    if check:
+        check_layer_decode(ws)
     return out, ids, p, offsets, perm, inv
+
+
+# ------------------------------------------------------------ measurement --
+
+def stream_read(buf, blocks_per_cu=8, sink=None):
+    """One streaming read of the CUDA tensor buf (qmoe_stream_read)."""
+    torch = _torch()
+    _cuda_contig(buf)
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=buf.device)
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib().qmoe_stream_read(_p(buf), nbytes, blocks_per_cu, _p(sink), _stream()),
+           "qmoe_stream_read")
+    return sink
 
 
 # -------------------------------------------------------------- profiling --

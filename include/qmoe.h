@@ -385,6 +385,18 @@ int moe_layer_decode(const qmoe_tier *tiers, int n_tiers, int E, int H, int F,
                      int32_t *inv_perm, float *y, void *ws, size_t ws_bytes,
                      void *stream);
 
+/* ------------------------------------------------------- measurement --
+ * qmoe_stream_read: reads `bytes` of device memory at buf once, with the
+ * decode kernels' access pattern (16-byte nontemporal vector loads,
+ * consecutive lanes on consecutive chunks, four loads in flight per lane,
+ * blocks_per_cu * CUs blocks of 256 threads), and writes at most one word to
+ * sink[0].  For measuring the HBM read rate the part sustains, the practical
+ * ceiling of a weight stream ([P3] section 4.4: decode reads every weight
+ * once per token).  buf 16-byte aligned, bytes % 16 == 0, 1 <= blocks_per_cu
+ * <= 64; sink a device word.                                              */
+int qmoe_stream_read(const void *buf, size_t bytes, int blocks_per_cu,
+                     uint32_t *sink, void *stream);
+
 /* ----------------------------------------------------------- profiling --
  * Optional per-kernel timing with HIP events recorded around every launch the
  * library makes while enabled (on the launch stream).  qmoe_profile_read

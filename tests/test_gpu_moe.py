@@ -117,11 +117,80 @@ def test_tiered_layer_full_size(T):
     _check_layer(configs.TIERED, T)
 
 
-def test_grouped_layer_full_size_sampled():
+def _check_all_tokens_sampled_cols(cfg, T, cols, seed=0, prefill=False, one_launch=False,
+                                   x=None):
+    """Every token of a full-size layer call against the oracle on the
+    sampled output columns `cols` (all columns of h, so every gate/up row is
+    checked through them).  The near-tie protocol of _check_layer applies;
+    the oracle runs one distinct expert per job on a process pool."""
+    import oracle_pool
+    layer = _layer(cfg)
+    if x is None:
+        x, xg = _x(cfg, T, seed)
+    else:
+        xg = to_gpu(x).to(torch.bfloat16) if cfg.x_dtype == "bf16" else to_gpu(x)
+    y, ws = layer.forward(xg, prefill=prefill, one_launch=one_launch)
+    y = to_np(y)
+    ids = to_np(ws["ids"])
+    Wr = to_np(layer.Wr)
+    b = None if layer.bias is None else to_np(layer.bias)
+    ids_ref, p_ref, lg_ref = moe.route(x, Wr, b, cfg.k, cfg.n_shared)
+    lg_bound = np.abs(x.astype(np.float64)) @ np.abs(Wr.astype(np.float64)).T
+    decided = moe.topk_gap(lg_ref, cfg.k) > 2 * 1e-5 * lg_bound.max(axis=1)
+    same = (ids == ids_ref).all(axis=1)
+    assert same[decided].all(), "routing differs on a token outside the near-tie margin"
+    rows = np.nonzero(same)[0]
+    assert rows.size >= T - max(1, T // 100), f"only {rows.size} of {T} tokens routed alike"
+    experts = np.unique(ids_ref[rows])
+
+    def jobs():
+        for e in experts:
+            ts = rows[(ids_ref[rows] == e).any(axis=1)]
+            t = cfg.tier_of(int(e))
+            wg, wu, wd = layer.expert_fp32(int(e))
+            yield (t.fmt_gate_up, wg, wu, t.fmt_down, np.ascontiguousarray(wd[cols]), x[ts])
+
+    outs = oracle_pool.run(oracle_pool.expert_job, jobs())
+    y_ref = np.zeros((T, len(cols)))
+    bound = np.zeros((T, len(cols)))
+    for e, (o, bo) in zip(experts, outs):
+        ts = rows[(ids_ref[rows] == e).any(axis=1)]
+        for j, t in enumerate(ts):
+            for i in np.nonzero(ids_ref[t] == e)[0]:
+                y_ref[t] += p_ref[t, i] * o[j]
+                bound[t] += p_ref[t, i] * bo[j]
+    assert_within_bound(y[rows][:, cols], y_ref[rows], bound[rows],
+                        what=f"{cfg.name} T={T} all tokens, {len(cols)} columns")
+    return layer, ws, rows
+
+
+def _grouped_x_with_all_row_counts(T=16):
+    """Decode rows of the grouped layer whose routing gives routed experts
+    with 1, 2 and at least 3 rows (the first seed that does): at hidden 7168
+    the dot-product blocking is 2 rows, so experts with 3 or more rows (and
+    the 16-row shared expert) take the matrix-core branch."""
+    cfg = configs.GROUPED
+    layer = _layer(cfg)
+    for seed in range(8):
+        x, xg = _x(cfg, T, seed)
+        _, ws = layer.forward(xg)
+        counts = np.diff(to_np(ws["offsets"]))[:cfg.E]
+        if (counts == 1).any() and (counts == 2).any() and (counts >= 3).any():
+            return x, seed
+    raise AssertionError("no seed gives experts with 1, 2 and >= 3 rows")
+
+
+def test_grouped_layer_full_size_all_tokens():
     """256 Q4_K experts + Q8_0 shared, hidden 7168, FFN 2048, 16 bf16 rows:
-    the oracle checks one token on 64 sampled output columns."""
+    all 16 tokens against the oracle on 64 sampled output columns, with a
+    routing that exercises the one-row and two-row dot products and the
+    matrix-core branch (experts with >= 3 rows, the shared expert)."""
+    x, seed = _grouped_x_with_all_row_counts()
     cols = np.sort(np.random.default_rng(0).choice(7168, 64, replace=False))
-    _check_layer(configs.GROUPED, 16, rows_checked=[5], cols=cols)
+    _, ws, rows = _check_all_tokens_sampled_cols(configs.GROUPED, 16, cols, x=x)
+    counts = np.diff(to_np(ws["offsets"]))
+    assert counts[configs.GROUPED.E] == 16       # the shared expert sees every row
+    assert rows.size == 16
 
 
 def test_ffn_and_combine_isolated_with_sentinels_and_duplicates():
@@ -238,11 +307,11 @@ def test_prefill_matches_decode_path():
     assert np.abs(yd - yp).max() <= 2e-2 * scale
 
 
-def test_prefill_chunk_full_size_sampled():
-    """2048 tokens through the 512-expert tiered layer on the matrix cores;
-    the oracle checks 35 sampled tokens on all 2048 outputs."""
-    rows = np.concatenate([np.arange(0, 2048, 64), [1, 2046, 2047]])
-    _check_layer(configs.PREFILL, 2048, rows_checked=rows, prefill=True)
+def test_prefill_chunk_full_size_all_tokens():
+    """2048 tokens through the 512-expert tiered layer on the matrix cores:
+    every token against the oracle on 64 sampled output columns."""
+    cols = np.sort(np.random.default_rng(3).choice(2048, 64, replace=False))
+    _check_all_tokens_sampled_cols(configs.PREFILL, 2048, cols, prefill=True)
 
 
 # ------------------------------------------------ one-launch decode layer --
@@ -285,12 +354,14 @@ def test_one_launch_layer_equals_separate_calls_bitexactly(cfg, T):
     assert _counter_words(ws) == []
 
 
-def test_one_launch_grouped_full_size_sampled():
+def test_one_launch_grouped_full_size_all_tokens():
     """The 16-row grouped layer in one launch (hidden 7168: the dot-product
-    blocking drops to 2 rows, so the shared expert runs on the matrix cores
-    in both phases)."""
+    blocking drops to 2 rows, so the shared expert and experts with 3 or more
+    rows run on the matrix cores in both phases): all 16 tokens on 64
+    sampled columns."""
+    x, _ = _grouped_x_with_all_row_counts()
     cols = np.sort(np.random.default_rng(1).choice(7168, 64, replace=False))
-    _check_layer(configs.GROUPED, 16, rows_checked=[2, 11], cols=cols, one_launch=True)
+    _check_all_tokens_sampled_cols(configs.GROUPED, 16, cols, x=x, one_launch=True)
 
 
 def test_one_launch_repeated_calls_reuse_the_counter():

@@ -241,24 +241,99 @@ def test_prefill_mx_tier_exact_gate_up(name, H, F, T):
     assert checked > 0
 
 
-@pytest.mark.parametrize("name,H,F", MX_SHAPES, ids=[m[0] for m in MX_SHAPES])
-def test_prefill_mx_tier_realistic_statistics(name, H, F):
-    """Context, not parity (the exact-g/u test above carries parity): on
-    realistic weights and activations, h's codes and block scales near a tie
-    depend on rounding inside the matrix cores, and with F = 64 (two blocks
-    per row) one such valid alternative moves an output by many times the
-    1e-3 bound.  Typical outputs stay well inside it: 98 % within, median
-    below a fifth of it."""
+def _silu_range(a, b):
+    """Range of SiLU over [a, b] (elementwise): SiLU falls until its minimum
+    at g* = -1.27846... and rises after it."""
+    silu = lambda g: g / (1.0 + np.exp(-g))
+    gstar = -1.2784645427610738
+    lo = np.minimum(silu(a), silu(b))
+    lo = np.where((a < gstar) & (b > gstar), silu(gstar), lo)
+    return lo, np.maximum(silu(a), silu(b))
+
+
+def _q_mxfp8_signed(h, E):
+    """h quantized to E4M3 with the block exponent E (broadcast): monotone
+    non-decreasing in h."""
+    scale = np.ldexp(1.0, E)
+    mag = mx.e4m3_value(mx.e4m3_code_of_magnitude(np.abs(h) / scale)) * scale
+    return np.where(h < 0, -mag, mag)
+
+
+def _h_decision_slack(g, u, bg, bu, dbuf, H, F, gamma=2.0 ** -18, rel_h=1e-6):
+    """Computed slack for the MXFP8 decisions on h.  The device's g and u
+    are fp32 sums of exact products on the matrix cores, rounded at most
+    once per 32-value scale block (64 roundings at K = 2048), so they are
+    within gamma * sum |w q(x)| of the oracle's (gamma = 64 * 2^-24), and its
+    h = SiLU(g) u within rel_h |h| more.  So each h_j lies in an interval [lo_j, hi_j]; its block
+    exponent may be any exponent of a block maximum in the interval of block
+    maxima, and its quantized value anything between Q_E(lo_j) and Q_E(hi_j)
+    over those exponents (quantization is monotone).  Returns per output
+    sum_j |w_d[n, j]| * (that range's width), and the fraction of h elements
+    with more than one possible value."""
+    eg, eu = gamma * bg, gamma * bu
+    s_lo, s_hi = _silu_range(g - eg, g + eg)
+    c = np.stack([s_lo * (u - eu), s_lo * (u + eu), s_hi * (u - eu), s_hi * (u + eu)])
+    h_lo, h_hi = c.min(0), c.max(0)
+    h_lo = h_lo - rel_h * np.abs(h_lo)
+    h_hi = h_hi + rel_h * np.abs(h_hi)
+    R = g.shape[0]
+    mag_lo = np.where(h_lo > 0, h_lo, np.where(h_hi < 0, -h_hi, 0.0))
+    mag_hi = np.maximum(np.abs(h_lo), np.abs(h_hi))
+    blo = mag_lo.reshape(R, F // 32, 32).max(-1)
+    bhi = mag_hi.reshape(R, F // 32, 32).max(-1)
+
+    def exp_of(a):  # the stored scale's exponent: floor(log2 a) - 8, clamped
+        return np.clip(np.frexp(np.maximum(a, 1e-300))[1] - 1 - 8, -127, 127)
+
+    e_lo, e_hi = exp_of(blo), exp_of(bhi)
+    assert (e_hi - e_lo <= 1).all()
+    vmin = np.full_like(h_lo, np.inf)
+    vmax = np.full_like(h_lo, -np.inf)
+    for e_b in (e_lo, e_hi):
+        E = np.repeat(e_b, 32, axis=1)
+        vmin = np.minimum(vmin, _q_mxfp8_signed(h_lo, E))
+        vmax = np.maximum(vmax, _q_mxfp8_signed(h_hi, E))
+    spread = vmax - vmin
+    wd = fm.dequantize("mxfp4", dbuf, H, F)
+    return spread @ np.abs(wd).T, float((spread > 0).mean())
+
+
+MX_REAL_SHAPES = MX_SHAPES + [("mx_tail_tier", 2048, 640)]
+
+
+@pytest.mark.parametrize("name,H,F", MX_REAL_SHAPES, ids=[m[0] for m in MX_REAL_SHAPES])
+def test_prefill_mx_tier_realistic_elementwise(name, H, F):
+    """MXFP4/MXFP4 experts on realistic weights and activations, up to the
+    tail tier's real shape (hidden 2048, FFN 640): every output within 1e-3
+    of sum |w_d q(h)| plus the computed slack of h's MXFP8 decisions near a
+    rounding or scale boundary (_h_decision_slack); the other tiers equal
+    qgemm_grouped_prefill bit for bit.  x's own MXFP8 codes are decided in
+    fp32 on both sides, identically."""
     T = 150
     host, dev = _mx_bank(H, F, 9, exact_gate_up=False)
     x = synth.normal((T, H), 1.0, 3, synth.ACT, T)
     o16, omx, off, pm, k = _run_mx_prefill(H, F, T, x, dev)
-    ratios = []
-    for e in (8, 9):
+    checked, choice = 0, []
+    for e in range(10):
         rows = np.arange(off[e], off[e + 1])
+        if rows.size == 0:
+            continue
+        if e < 8:
+            assert_bitexact(omx[rows], o16[rows], f"{name} expert {e} (fp16 path)")
+            continue
         gs, us, ds = host[2]
-        ref, bound = mx.mx_expert_ffn(gs[e - 8], us[e - 8], ds[e - 8], H, F,
-                                      x[pm[rows] // k].astype(np.float64))
-        ratios.append((np.abs(omx[rows] - ref) / (1e-3 * bound)).ravel())
-    r = np.concatenate(ratios)
-    assert np.mean(r <= 1) >= 0.98 and np.median(r) < 0.2, (np.mean(r <= 1), np.median(r))
+        gbuf, ubuf, dbuf = gs[e - 8], us[e - 8], ds[e - 8]
+        X = x[pm[rows] // k].astype(np.float64)
+        ref, bound = mx.mx_expert_ffn(gbuf, ubuf, dbuf, H, F, X)
+        g, bg = mx.mx_gemm(gbuf, F, H, X)
+        u, bu = mx.mx_gemm(ubuf, F, H, X)
+        slack, frac = _h_decision_slack(g, u, bg, bu, dbuf, H, F)
+        choice.append(frac)
+        err = np.abs(omx[rows] - ref)
+        lim = 1e-3 * bound + slack
+        assert (err <= lim).all(), f"{name} mx expert {e}: worst ratio {(err / lim).max():.3g}"
+        # the slack is not what carries the comparison: most outputs have none
+        assert np.median(slack / bound) < 1e-3, np.median(slack / bound)
+        checked += rows.size
+    assert checked > 0
+    assert max(choice) < 0.05, choice
