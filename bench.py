@@ -77,54 +77,149 @@ def step_calls(tiered, grouped, xt, xg, s):
     return [(tiered, x1, s % 4, 1), (tiered, x6, (s + 2) % 4, 6), (grouped, x16, s % 2, 16)]
 
 
-def cpu_baseline(budget_s=20.0):
-    """The oracle (float64 NumPy) on the tiered layer at 1 row, on a bounded
-    sample of tokens: per token, dequantize-then-dot of its 10 experts and the
-    router.  Inputs are quantized by the oracle (untimed)."""
-    from decode_moe_mul_amd import configs, synth
-    from oracle import formats as fm
-    from oracle import moe
+def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        return max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
-        blas_threads = 1
-    cfg = configs.TIERED
+        return 1
+
+
+def _threads(n):
+    """Context limiting the BLAS pool to n threads (None: unchanged)."""
+    import contextlib
+    if n is None:
+        return contextlib.nullcontext()
+    from threadpoolctl import threadpool_limits
+    return threadpool_limits(n)
+
+
+_ORACLE_EXPERTS = {}   # oracle-quantized experts per layer, shared by the timed runs
+_ORACLE_DENSE = []
+
+
+def _oracle_moe_rate(cfg, T, budget_s, threads=None, seed=2, max_experts=None):
+    """The oracle on layer calls of T rows of cfg: route (router GEMV, top-k,
+    softmax) then dequantize-then-dot of each selected expert, timed per call
+    over distinct row sets until budget_s is spent.  Weights are drawn on the
+    host with the same shapes and distributions as the device layers and
+    quantized by the oracle (untimed).  With max_experts, each call evaluates
+    only that many of its distinct experts and the call time is scaled by
+    (distinct experts) / (evaluated), as is the byte count (a bounded sample
+    of a call too long to run whole)."""
+    from decode_moe_mul_amd import synth
+    from oracle import formats as fm
+    from oracle import moe
     Wr = synth.normal((cfg.E, cfg.H), cfg.sigma_router, 0, synth.ROUTER, 0)
-    b = synth.rank_prior(cfg.E, cfg.prior_lambda)
-    x = synth.normal((64, cfg.H), 1.0, 2, synth.ACT, 0)
-    cache = {}
+    b = None if cfg.prior_lambda is None else synth.rank_prior(cfg.E, cfg.prior_lambda)
+    cache = _ORACLE_EXPERTS.setdefault(cfg.name, {})
 
     def expert(e):
         if e not in cache:
             t = cfg.tier_of(e)
-            w = [synth.normal((cfg.F, cfg.H), cfg.sigma_w, 0, tag, e) for tag in (synth.GATE, synth.UP)]
-            wd = synth.normal((cfg.H, cfg.F), cfg.sigma_w, 0, synth.DOWN, e)
-            cache[e] = (t.fmt_gate_up, fm.quantize(t.fmt_gate_up, w[0]),
-                        fm.quantize(t.fmt_gate_up, w[1]), t.fmt_down, fm.quantize(t.fmt_down, wd))
+            tags = ((synth.GATE, synth.UP, synth.DOWN) if e < cfg.E
+                    else (synth.SH_GATE, synth.SH_UP, synth.SH_DOWN))
+            idx = e if e < cfg.E else e - cfg.E
+            wg = synth.normal((cfg.F, cfg.H), cfg.sigma_w, 0, tags[0], idx)
+            wu = synth.normal((cfg.F, cfg.H), cfg.sigma_w, 0, tags[1], idx)
+            wd = synth.normal((cfg.H, cfg.F), cfg.sigma_w, 0, tags[2], idx)
+            cache[e] = (t.fmt_gate_up, fm.quantize(t.fmt_gate_up, wg),
+                        fm.quantize(t.fmt_gate_up, wu), t.fmt_down, fm.quantize(t.fmt_down, wd))
         return cache[e]
 
     def ebytes(e):
         t = cfg.tier_of(e)
-        return 2 * fm.tensor_bytes(t.fmt_gate_up, cfg.F, cfg.H) + fm.tensor_bytes(t.fmt_down, cfg.H, cfg.F)
+        return (2 * fm.tensor_bytes(t.fmt_gate_up, cfg.F, cfg.H)
+                + fm.tensor_bytes(t.fmt_down, cfg.H, cfg.F))
 
-    done, elapsed, nbytes = 0, 0.0, 0
-    for t in range(x.shape[0]):
-        ids, p, _ = moe.route(x[t:t + 1], Wr, b, cfg.k)       # untimed: quantize its experts
-        for e in ids[0]:
-            expert(int(e))
-        t0 = time.perf_counter()
-        ids, p, _ = moe.route(x[t:t + 1], Wr, b, cfg.k)
-        moe.moe_layer(x[t:t + 1], ids, p, expert, cfg.H, cfg.F, cfg.E)
-        elapsed += time.perf_counter() - t0
-        nbytes += cfg.E * cfg.H * 4 + sum(ebytes(int(e)) for e in np.unique(ids))
-        done += 1
-        if elapsed > budget_s:
-            break
-    return {"value": round(nbytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": int(blas_threads),
-            "kind": "oracle",
-            "sample": f"tiered 512-expert layer at 1 row, {done} tokens, float64 NumPy "
-                      f"dequantize-then-dot ({elapsed:.1f}s; {done / elapsed:.2f} tokens/s)"}
+    calls, elapsed, nbytes, tokens = 0, 0.0, 0.0, 0
+    with _threads(threads):
+        for c in range(1 << 20):
+            x = synth.normal((T, cfg.H), 1.0, seed, synth.ACT, c)
+            if cfg.x_dtype == "bf16":
+                x = synth.bf16_round(x)
+            ids, p, _ = moe.route(x, Wr, b, cfg.k, cfg.n_shared)   # untimed: pick experts
+            distinct = [int(e) for e in np.unique(ids)]
+            use = distinct if max_experts is None else distinct[:max_experts]
+            for e in use:
+                expert(e)
+            t0 = time.perf_counter()
+            ids, p, _ = moe.route(x, Wr, b, cfg.k, cfg.n_shared)
+            t_route = time.perf_counter() - t0
+            t0 = time.perf_counter()
+            if max_experts is None:
+                moe.moe_layer(x, ids, p, expert, cfg.H, cfg.F, cfg.E_total)
+            else:
+                for e in use:
+                    ts = np.nonzero((ids == e).any(axis=1))[0]
+                    moe.expert_ffn(expert(e), cfg.H, cfg.F, x[ts])
+            t_exp = (time.perf_counter() - t0) * len(distinct) / len(use)
+            elapsed += t_route + t_exp
+            nbytes += cfg.E * cfg.H * 4 + sum(ebytes(e) for e in distinct)
+            tokens += T
+            calls += 1
+            if elapsed > budget_s:
+                break
+    return {"threads": threads or _blas_threads(), "calls": calls,
+            "s_per_call": round(elapsed / calls, 4),
+            "gbs": round(nbytes / elapsed / 1e9, 4),
+            "tokens_per_s": round(tokens / elapsed, 3)}
+
+
+def _oracle_dense_rate(budget_s, threads=None):
+    """The oracle on the Llama-3-8B layer's seven quantized matrices at one
+    row (dequantize-then-dot per matrix)."""
+    from decode_moe_mul_amd import configs, synth
+    from oracle import formats as fm
+    from oracle import moe
+    if not _ORACLE_DENSE:
+        for i, (name, N, K, fmt) in enumerate(configs.LLAMA8B_GEMV.mats):
+            _ORACLE_DENSE.append((fmt, fm.quantize(fmt, synth.normal((N, K), 0.02, 0, synth.DENSE, i)),
+                                  N, K))
+    mats = _ORACLE_DENSE
+    nbytes = sum(fm.tensor_bytes(f, N, K) for f, _, N, K in mats)
+    calls, elapsed = 0, 0.0
+    with _threads(threads):
+        while elapsed < budget_s:
+            xs = {K: synth.normal((1, K), 1.0, 3, synth.ACT, 100 * calls + K) for K in (4096, 14336)}
+            t0 = time.perf_counter()
+            for f, buf, N, K in mats:
+                moe.gemv(f, buf, N, K, xs[K])
+            elapsed += time.perf_counter() - t0
+            calls += 1
+    return {"threads": threads or _blas_threads(), "calls": calls,
+            "s_per_call": round(elapsed / calls, 4),
+            "gbs": round(nbytes * calls / elapsed / 1e9, 4),
+            "tokens_per_s": round(calls / elapsed, 3)}
+
+
+def cpu_baseline(budget_s=8.0):
+    """The oracle (float64 NumPy, as it stands) timed on this host's cores
+    on bounded samples of every workload; the headline `value` is the tiered
+    layer at 1 row (the decode config the bench's first call uses), with the
+    BLAS pool at its default size.  C1-C3 are also timed on one thread."""
+    from decode_moe_mul_amd import configs
+    cores = _blas_threads()
+    cfgs = {}
+    t3 = _oracle_moe_rate(configs.TIERED, 1, budget_s)
+    cfgs["tiered_1row"] = t3
+    cfgs["tiered_1row"]["single_thread"] = _oracle_moe_rate(configs.TIERED, 1, budget_s / 4, 1)
+    cfgs["tiered_6rows"] = _oracle_moe_rate(configs.TIERED, 6, budget_s / 4)
+    cfgs["tiered_6rows"]["single_thread"] = _oracle_moe_rate(configs.TIERED, 6, budget_s / 4, 1)
+    cfgs["tiny_4rows"] = _oracle_moe_rate(configs.TINY, 4, 1.0)
+    cfgs["tiny_4rows"]["single_thread"] = _oracle_moe_rate(configs.TINY, 4, 1.0, 1)
+    cfgs["dense_gemv_1row"] = _oracle_dense_rate(budget_s / 4)
+    cfgs["dense_gemv_1row"]["single_thread"] = _oracle_dense_rate(budget_s / 4, 1)
+    cfgs["grouped_16rows"] = _oracle_moe_rate(configs.GROUPED, 16, budget_s / 4, max_experts=3)
+    cfgs["grouped_16rows"]["sample"] = "3 of the distinct experts of each call, scaled"
+    cfgs["prefill_2048rows"] = _oracle_moe_rate(configs.PREFILL, 2048, budget_s / 4,
+                                                max_experts=12)
+    cfgs["prefill_2048rows"]["sample"] = "12 of the distinct experts of the chunk, scaled"
+    return {"value": t3["gbs"], "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"tiered 512-expert layer at 1 row, {t3['calls']} calls, float64 NumPy "
+                      f"dequantize-then-dot ({t3['s_per_call']} s per call; "
+                      f"{t3['tokens_per_s']} tokens/s); every workload in `configs`",
+            "configs": cfgs}
 
 
 # ------------------------------------------------------------------ traffic --
@@ -249,6 +344,70 @@ def summarize_pmc(fetch_dir, write_dir):
     with open(TRAFFIC_FILE, "w") as fh:
         json.dump(out, fh, indent=1)
     print(json.dumps(out, indent=1))
+
+
+def summarize_prefill_pmc(dirs):
+    """Markdown table of rocprofv3 --pmc runs of `bench.py --prefill-only`:
+    per prefill kernel (pass 1 = gate/up, pass 2 = down; the row-tile class
+    in the template arguments) the launches and the average of every counter
+    per dispatch; FETCH_SIZE / WRITE_SIZE scaled to bytes by the run's 256 MiB
+    calibration copy; the MFMA busy fraction as SQ_VALU_MFMA_BUSY_CYCLES /
+    (GRBM_GUI_ACTIVE x CUs x 4 SIMDs) when both were collected."""
+    import collections
+    import re
+    rows = []
+    for d in dirs:
+        rows += _pmc_rows(d)
+
+    def group(name):
+        n = re.sub(r"^void ", "", name).replace("qmoe::", "")
+        m = re.match(r"(\w+)(<[^>]*>)?", n)
+        return m.group(1) + (m.group(2) or "")
+
+    keep = ("prefill", "router_gemm", "topk", "permute", "combine")
+    per = collections.defaultdict(lambda: collections.defaultdict(dict))
+    for r in rows:
+        k = group(r["Kernel_Name"])
+        key = r.get("Dispatch_Id") or r.get("Correlation_Id")
+        c = r["Counter_Name"]
+        per[k][c][key] = per[k][c].get(key, 0.0) + float(r["Counter_Value"])
+    cal = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        cp = {}
+        for k, cs in per.items():
+            if "copyBuffer" in k and c in cs:
+                cp.update(cs[c])
+        if cp:
+            cal[c] = CAL_BYTES / (cp[max(cp, key=int)] * 1024)   # bytes per counted byte
+    counters = sorted({c for k, cs in per.items() for c in cs})
+    print("| kernel | launches | " + " | ".join(counters) + " |")
+    print("|---|---:|" + "---:|" * len(counters))
+    for k in sorted(per):
+        if not any(p in k for p in keep):
+            continue
+        cs = per[k]
+        n = max(len(v) for v in cs.values())
+        vals = []
+        for c in counters:
+            v = cs.get(c)
+            vals.append("" if not v else f"{sum(v.values()) / len(v):.4g}")
+        print(f"| {k} | {n} | " + " | ".join(vals) + " |")
+    print()
+    cus = 256
+    for k in sorted(per):
+        if not k.startswith("prefill_kernel"):
+            continue
+        cs = per[k]
+        line = [k]
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            if c in cs and c in cal:
+                b = sum(cs[c].values()) / len(cs[c]) * 1024 * cal[c]
+                line.append(f"{c} {b / 1e6:.1f} MB per launch")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in cs and "GRBM_GUI_ACTIVE" in cs:
+            busy = sum(cs["SQ_VALU_MFMA_BUSY_CYCLES"].values())
+            act = sum(cs["GRBM_GUI_ACTIVE"].values())
+            line.append(f"MFMA busy {busy / (act * cus * 4):.4f} of GRBM_GUI_ACTIVE x {cus} CUs x 4")
+        print("- " + "; ".join(line))
 
 
 def _events_ms(torch, fn, n):
@@ -476,6 +635,64 @@ def prefill_chunk(torch, calls=10):
                              "kernel_ms": {k: round(v, 4) for k, v in mx_kern.items()}}}
 
 
+# names of the kernels the library records for one decode layer call
+DECODE_KERNELS = ("route_decode", "router_gemv", "topk", "permute", "ffn_gate_up", "ffn_down",
+                  "ffn_down_combine", "combine")
+
+
+def stream_ceiling(torch, reps=20):
+    """The HBM read rate of a plain streaming read (qmoe_stream_read: the
+    decode kernels' 16-byte nontemporal loads) over a 2 GiB buffer, best of
+    4 / 8 / 16 blocks per CU: the practical ceiling of a weight stream."""
+    from decode_moe_mul_amd import qmoe
+    nbytes = 2 << 30
+    buf = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda").fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = {"bytes": nbytes, "per_blocks_per_cu": {}}
+    for bpc in (4, 8, 16):
+        qmoe.stream_read(buf, bpc, sink)
+        ms = _events_ms(torch, lambda i: qmoe.stream_read(buf, bpc, sink), reps)
+        out["per_blocks_per_cu"][str(bpc)] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    best = max(out["per_blocks_per_cu"].values())
+    out["gbs"] = best
+    out["frac_of_peak"] = round(best / HBM_PEAK_GBS, 4)
+    del buf
+    torch.cuda.empty_cache()
+    log(f"streaming-read ceiling: {best} GB/s")
+    return out
+
+
+def graph_replay(torch, calls, iters=500, warm=50):
+    """Each decode call captured as a HIP graph (torch.cuda.CUDAGraph around
+    the library calls) and replayed on one stream: `warm` untimed replays,
+    then `iters` timed ones with an event before each, rotating through the
+    captured calls (distinct weight copies and input rows).  Returns the
+    per-replay times in us (median, p10, p90)."""
+    graphs = []
+    for layer, x, copy, rows in calls:
+        layer.forward(x, copy)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            layer.forward(x, copy)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for i in range(warm):
+        graphs[i % len(graphs)].replay()
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
+    torch.cuda.synchronize()
+    for i in range(iters):
+        ev[i].record(stream)
+        graphs[i % len(graphs)].replay()
+    ev[iters].record(stream)
+    torch.cuda.synchronize()
+    us = np.array([ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(iters)])
+    del graphs
+    return {"iters": iters, "median_us": round(float(np.median(us)), 2),
+            "p10_us": round(float(np.percentile(us, 10)), 2),
+            "p90_us": round(float(np.percentile(us, 90)), 2)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -483,17 +700,27 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-only", action="store_true",
-                    help="skip the dense-GEMV and prefill sections (counter runs)")
+                    help="skip the dense-GEMV, prefill, MX and int8 sections (counter runs)")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="run only the 2048-row prefill section (prefill counter runs)")
+    ap.add_argument("--one-launch", action="store_true",
+                    help="also time the retired one-launch layer (a cooperative launch)")
+    ap.add_argument("--graph-iters", type=int, default=500)
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
                     help="print the per-kernel table of a rocprofv3 --kernel-trace run and exit")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the traffic summary from two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--summarize-prefill-pmc", nargs="+", metavar="PMC_DIR",
+                    help="print the prefill kernels' counter table of rocprofv3 --pmc runs and exit")
     a = ap.parse_args()
     if a.summarize_pmc:
         summarize_pmc(*a.summarize_pmc)
         return
     if a.summarize_trace:
         summarize_trace(a.summarize_trace)
+        return
+    if a.summarize_prefill_pmc:
+        summarize_prefill_pmc(a.summarize_prefill_pmc)
         return
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; the decode path has "
@@ -505,21 +732,29 @@ def main():
 
     torch.cuda.set_device(0)
     qmoe.lib()
+    if a.prefill_only:
+        cal_src = torch.empty(CAL_BYTES // 4, dtype=torch.float32, device="cuda")
+        torch.empty_like(cal_src).copy_(cal_src)
+        torch.cuda.synchronize()
+        del cal_src
+        print(json.dumps({"prefill": prefill_chunk(torch)}), flush=True)
+        return
     tiered, grouped, xt, xg = build_workload(torch)
     stream = torch.cuda.current_stream()
+    ROWS = (1, 6, 16)
 
     # algorithmic bytes per call (routing is deterministic: take it from one pass)
-    per_step_bytes, gate_up_bytes = [], []
+    call_bytes = np.zeros((a.steps, 3))
+    gate_up_bytes = []
     for s in range(a.steps):
-        b_step, g_step = 0, 0
-        for layer, x, copy, rows in step_calls(tiered, grouped, xt, xg, s):
+        g_step = 0
+        for i, (layer, x, copy, rows) in enumerate(step_calls(tiered, grouped, xt, xg, s)):
             _, ws = layer.forward(x, copy)
             ids = ws["ids"].cpu().numpy()
-            b_step += layer.weight_bytes(ids)
+            call_bytes[s, i] = layer.weight_bytes(ids)
             flat = np.unique(ids)
             g_step += sum(2 * qmoe.tensor_bytes(layer.cfg.tier_of(int(e)).fmt_gate_up,
                                                 layer.cfg.F, layer.cfg.H) for e in flat)
-        per_step_bytes.append(b_step)
         gate_up_bytes.append(g_step)
 
     # calibration copy for the traffic counters (outside the timed region)
@@ -546,47 +781,87 @@ def main():
         t0.record(stream)
         for s in range(a.steps):
             for layer, x, copy, rows in calls_of_step(s):
-                layer.forward(x, copy, one_launch=one_launch)
+                layer.forward(x, copy, one_launch=one_launch, check=False)
         t1.record(stream)
         torch.cuda.synchronize()
         log(f"timed {tag}: {t0.elapsed_time(t1) / a.steps:.4f} ms per step")
         return t0.elapsed_time(t1)
 
+    def kernel_ms(calls_of_step, names):
+        """Summed duration of the library's launches (HIP events around every
+        launch, on its stream) over a.steps steps, per kernel name."""
+        qmoe.profile_reset()
+        qmoe.profile_enable(True)
+        timed(calls_of_step, "all-kernel events")
+        qmoe.profile_enable(False)
+        return {k: qmoe.profile_read(k) for k in names}
+
+    one_call = lambda i: (lambda s: [step_calls(tiered, grouped, xt, xg, s)[i]])
+    whole_step = lambda s: step_calls(tiered, grouped, xt, xg, s)
+
     # 1. the step (value, ms_per_step): the three calls, nothing recorded
     #    between kernels
-    total_ms = timed(lambda s: step_calls(tiered, grouped, xt, xg, s), "step")
+    total_ms = timed(whole_step, "step")
     ms_step = total_ms / a.steps
     # 2. each row count on its own, same inputs and weight rotation
-    call_ms = np.array([timed(lambda s, i=i: [step_calls(tiered, grouped, xt, xg, s)[i]],
-                              f"rows={r}") for i, r in enumerate((1, 6, 16))])
+    call_ms = np.array([timed(one_call(i), f"rows={r}") for i, r in enumerate(ROWS)])
     # 3. the dominant kernel: library HIP events around every gate/up launch
     #    (recorded on the launch stream) over the same steps
     qmoe.profile_reset()
     qmoe.profile_only("ffn_gate_up")
     qmoe.profile_enable(True)
-    timed(lambda s: step_calls(tiered, grouped, xt, xg, s), "gate/up events")
+    timed(whole_step, "gate/up events")
     qmoe.profile_enable(False)
     qmoe.profile_only(None)
     n_gu, gu_ms = qmoe.profile_read("ffn_gate_up")
-    # 4. every kernel's time (events around all launches; reported only)
-    qmoe.profile_reset()
-    qmoe.profile_enable(True)
-    timed(lambda s: step_calls(tiered, grouped, xt, xg, s), "all-kernel events")
-    qmoe.profile_enable(False)
-    kernel_ms = {k: qmoe.profile_read(k) for k in
-                 ("route_decode", "router_gemv", "topk", "permute", "ffn_gate_up", "ffn_down",
-                  "combine")}
+    # 4. every kernel's time over the step, and per row count the layer's
+    #    summed kernel time (the 70 % bar is judged on it)
+    step_kernels = kernel_ms(whole_step, DECODE_KERNELS)
+    call_kernel_ms = []
+    for i in range(3):
+        ks = kernel_ms(one_call(i), DECODE_KERNELS)
+        call_kernel_ms.append(sum(v[1] for v in ks.values()) / a.steps)
+    # 5. graph replay of each call (>= 500 replays, median / p10 / p90)
+    graphs = {}
+    for i, r in enumerate(ROWS):
+        copies = 4 if i < 2 else 2
+        calls = [step_calls(tiered, grouped, xt, xg, s)[i] for s in range(copies)]
+        graphs[str(r)] = graph_replay(torch, calls, a.graph_iters)
+        log(f"graph replay rows={r}: {graphs[str(r)]}")
+    # 6. the retired one-launch layer (opt-in)
+    one_launch = None
+    if a.one_launch:
+        one_ms = np.array([timed(one_call(i), f"one launch rows={r}", one_launch=True)
+                           for i, r in enumerate((1, 6))])
+        for r in (1, 6):
+            tiered.check_one_launch(r)
+        one_launch = {"ms_per_call": {str(r): round(one_ms[i] / a.steps, 5)
+                                      for i, r in enumerate((1, 6))},
+                      "tokens_per_s": {str(r): round(r * a.steps / (one_ms[i] * 1e-3), 1)
+                                       for i, r in enumerate((1, 6))}}
 
-    # 5. the same 1- and 6-row calls as one cooperative launch each
-    #    (moe_layer_decode), same inputs and weight rotation
-    one_ms = np.array([timed(lambda s, i=i: [step_calls(tiered, grouped, xt, xg, s)[i]],
-                             f"one launch rows={r}", one_launch=True)
-                       for i, r in enumerate((1, 6))])
-    one_launch = {"ms_per_call": {str(r): round(one_ms[i] / a.steps, 5)
-                                  for i, r in enumerate((1, 6))},
-                  "tokens_per_s": {str(r): round(r * a.steps / (one_ms[i] * 1e-3), 1)
-                                   for i, r in enumerate((1, 6))}}
+    per_config = {}
+    mean_bytes = call_bytes.mean(axis=0)
+    for i, r in enumerate(ROWS):
+        wall = call_ms[i] / a.steps
+        kern = call_kernel_ms[i]
+        g = graphs[str(r)]
+        per_config[str(r)] = {
+            "layer": "tiered" if i < 2 else "grouped",
+            "weight_bytes_per_call": int(mean_bytes[i]),
+            "ms_per_call": round(wall, 5),
+            "tokens_per_s": round(r / (wall * 1e-3), 1),
+            "gbs": round(mean_bytes[i] / (wall * 1e-3) / 1e9, 1),
+            "hbm_frac": round(mean_bytes[i] / (wall * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "kernel_us_per_call": round(kern * 1e3, 2),
+            "kernel_gbs": round(mean_bytes[i] / (kern * 1e-3) / 1e9, 1),
+            "kernel_hbm_frac": round(mean_bytes[i] / (kern * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "meets_70pct_bar": bool(mean_bytes[i] / (kern * 1e-3) / 1e9 >= 0.7 * HBM_PEAK_GBS),
+            "graph_replay": dict(g, gbs_median=round(mean_bytes[i] / (g["median_us"] * 1e-6) / 1e9,
+                                                     1)),
+        }
 
+    ceiling = stream_ceiling(torch)
     dense = None if a.decode_only else dense_gemv(torch, a.steps)
     ternary = None if a.decode_only else ternary_gemv(torch, a.steps)
     prefill = None if a.decode_only else prefill_chunk(torch)
@@ -595,7 +870,7 @@ def main():
 
     t = stored_traffic()
     traffic = None if t is None else int(t["traffic_bytes_per_launch"])
-    total_bytes = float(np.sum(per_step_bytes))
+    total_bytes = float(call_bytes.sum())
     gbs = total_bytes / (total_ms * 1e-3) / 1e9
     gu_gbs = float(np.sum(gate_up_bytes)) / (gu_ms * 1e-3) / 1e9
     out = {
@@ -619,22 +894,26 @@ def main():
                    "weight_copies": {"tiered": 4, "grouped": 2}},
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "tokens_per_s": {str(r): round(r * a.steps / (call_ms[i] * 1e-3), 1)
-                         for i, r in enumerate((1, 6, 16))},
-        "ms_per_call": {str(r): round(call_ms[i] / a.steps, 5) for i, r in enumerate((1, 6, 16))},
+                         for i, r in enumerate(ROWS)},
+        "ms_per_call": {str(r): round(call_ms[i] / a.steps, 5) for i, r in enumerate(ROWS)},
+        "per_config": per_config,
         "weight_bytes_per_step": int(total_bytes / a.steps),
-        "kernel_ms_per_step": {k: round(v[1] / a.steps, 5) for k, v in kernel_ms.items()},
+        "kernel_ms_per_step": {k: round(v[1] / a.steps, 5) for k, v in step_kernels.items()
+                               if v[0]},
         "roofline": {"bound": "hbm", "kernel": "ffn_gate_up",
                      "achieved": round(gu_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "launches": n_gu,
                      "avg_launch_us": round(gu_ms * 1e3 / max(n_gu, 1), 3),
                      "algorithmic_bytes_per_launch": int(np.sum(gate_up_bytes) / max(n_gu, 1))},
+        "stream_read_ceiling": ceiling,
     }
     if dense is not None:
         out["dense_gemv"] = dense
     if ternary is not None:
         out["ternary_gemv"] = ternary
-    out["one_launch_layer"] = one_launch
+    if one_launch is not None:
+        out["one_launch_layer"] = one_launch
     if prefill is not None:
         out["prefill"] = prefill
     if mx is not None:
@@ -642,7 +921,7 @@ def main():
     if i8 is not None:
         out["int8_gemv"] = i8
     if not a.no_cpu_baseline:
-        log("timing the CPU oracle on a bounded sample ...")
+        log("timing the CPU oracle on bounded samples ...")
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)
 

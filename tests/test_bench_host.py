@@ -63,3 +63,30 @@ def test_trace_table_groups_by_kernel_and_grid(tmp_path, capsys):
     assert body[0].split("|")[1].strip().startswith("ffn_gate_up") and int(body[0].split("|")[2]) == 100
     assert "ffn_gate_up: 3 launches, average 207.333 us" in out
     assert "ffn_down: 1 launches, average 5.000 us" in out
+
+
+def test_prefill_counter_summary(tmp_path, capsys):
+    """Counters averaged per dispatch per prefill kernel; FETCH_SIZE scaled by
+    the 256 MiB calibration copy; MFMA busy fraction from the two counters."""
+    d = tmp_path / "pmc"
+    d.mkdir()
+    pk = "void qmoe::prefill_kernel<1, 1, 8, false>(qmoe::PrefillParams, int)"
+    cp = "__amd_rocclr_copyBuffer"
+    rows = [(cp, 1, "FETCH_SIZE", 131072.0),                  # 256 MiB read -> 128 Ki
+            (pk, 2, "FETCH_SIZE", 1000.0), (pk, 3, "FETCH_SIZE", 3000.0),
+            (pk, 2, "SQ_VALU_MFMA_BUSY_CYCLES", 1024.0 * 0.5), (pk, 2, "GRBM_GUI_ACTIVE", 1.0),
+            (pk, 3, "SQ_VALU_MFMA_BUSY_CYCLES", 1024.0 * 0.5), (pk, 3, "GRBM_GUI_ACTIVE", 1.0)]
+    with open(d / "x_counter_collection.csv", "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name",
+                                           "Counter_Value"])
+        w.writeheader()
+        for name, disp, c, v in rows:
+            w.writerow({"Dispatch_Id": disp, "Kernel_Name": name, "Counter_Name": c,
+                        "Counter_Value": v})
+    bench.summarize_prefill_pmc([str(d)])
+    out = capsys.readouterr().out
+    line = [l for l in out.splitlines() if l.startswith("| prefill_kernel")][0]
+    assert "| 2 |" in line and "2000" in line
+    # 2000 KiB per launch x 2 (the copy read 256 MiB as 128 Ki units) = 4096000 B
+    assert "FETCH_SIZE 4.1 MB per launch" in out
+    assert "MFMA busy 0.5000" in out
