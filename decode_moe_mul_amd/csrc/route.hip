@@ -13,6 +13,8 @@
 //  topk_kernel         one wave per row: sums the split-K partials in fixed
 //                      order, adds the bias, selects k by repeated wave
 //                      arg-max, softmax over the kept logits.
+#include <mutex>
+
 #include "route.hpp"
 
 namespace qmoe {
@@ -276,36 +278,46 @@ size_t moe_route_decode_workspace_size(int T, int H, int E) {
   return kDecodeCtrBytes + round_up256((size_t)KS * T * E * sizeof(float));
 }
 
-int moe_route_decode(const void* x, int x_dtype, int T, int H, const float* Wr,
-                     const float* bias, int E, int k, int n_shared, int32_t* ids, float* p,
-                     float* logits, int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* ws,
-                     size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace qmoe {
+
+__global__ void zero_words_kernel(unsigned* w, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) w[i] = 0u;
+}
+
+// moe_route_decode on the workspace ws; `who` names the entry point in error
+// texts; clear_ctr: zero the block counter first (one small kernel).
+static int route_decode_impl(const char* who, const void* x, int x_dtype, int T, int H,
+                             const float* Wr, const float* bias, int E, int k, int n_shared,
+                             int32_t* ids, float* p, float* logits, int32_t* offsets,
+                             int32_t* perm, int32_t* inv_perm, void* ws, size_t ws_bytes,
+                             bool clear_ctr, void* stream) {
   if (T < 0 || H <= 0 || E <= 0 || k < 1 || k > E || k > 64 || n_shared < 0)
-    return fail(QMOE_ERR_INVALID_ARG,
-                "moe_route_decode: bad sizes T=%d H=%d E=%d k=%d n_shared=%d", T, H, E, k,
-                n_shared);
+    return fail(QMOE_ERR_INVALID_ARG, "%s: bad sizes T=%d H=%d E=%d k=%d n_shared=%d", who, T,
+                H, E, k, n_shared);
   if (T > kGemvRowsMax)
-    return fail(QMOE_ERR_UNSUPPORTED, "moe_route_decode: T=%d > %d rows", T, kGemvRowsMax);
-  if (E > 512) return fail(QMOE_ERR_UNSUPPORTED, "moe_route_decode: E=%d > 512", E);
-  if (H % 4) return fail(QMOE_ERR_INVALID_ARG, "moe_route_decode: H %% 4 != 0");
+    return fail(QMOE_ERR_UNSUPPORTED, "%s: T=%d > %d rows", who, T, kGemvRowsMax);
+  if (E > 512) return fail(QMOE_ERR_UNSUPPORTED, "%s: E=%d > 512", who, E);
+  if (H % 4) return fail(QMOE_ERR_INVALID_ARG, "%s: H %% 4 != 0", who);
   if (x_dtype != QMOE_F32 && x_dtype != QMOE_BF16)
-    return fail(QMOE_ERR_UNSUPPORTED, "moe_route_decode: unknown x_dtype %d", x_dtype);
+    return fail(QMOE_ERR_UNSUPPORTED, "%s: unknown x_dtype %d", who, x_dtype);
   const int kt = k + n_shared, E_total = E + n_shared, A = T * kt;
   const int hist_ints = kDecodeLdsInts - ((A + 63) & ~63) - kGemvBlock / 64;
   if (hist_ints < E_total)
-    return fail(QMOE_ERR_UNSUPPORTED, "moe_route_decode: T*(k+n_shared)=%d with %d experts "
-                "does not fit the fused permutation", A, E_total);
-  if (!offsets) return fail(QMOE_ERR_INVALID_ARG, "moe_route_decode: null offsets");
+    return fail(QMOE_ERR_UNSUPPORTED, "%s: T*(k+n_shared)=%d with %d experts "
+                "does not fit the fused permutation", who, A, E_total);
+  if (!offsets) return fail(QMOE_ERR_INVALID_ARG, "%s: null offsets", who);
   if (T == 0)  // nothing to route; the empty permutation still zeroes offsets
     return moe_permute(nullptr, 0, kt, E_total, offsets, nullptr, nullptr, stream);
   if (!x || !Wr || !ids || !p || !perm || !inv_perm)
-    return fail(QMOE_ERR_INVALID_ARG, "moe_route_decode: null pointer");
+    return fail(QMOE_ERR_INVALID_ARG, "%s: null pointer", who);
   if (!QMOE_ALIGNED(x, 16) || !QMOE_ALIGNED(Wr, 16))
-    return fail(QMOE_ERR_INVALID_ARG, "moe_route_decode: misaligned x/Wr");
+    return fail(QMOE_ERR_INVALID_ARG, "%s: misaligned x/Wr", who);
   const size_t need = moe_route_decode_workspace_size(T, H, E);
   if (!ws || ws_bytes < need || !QMOE_ALIGNED(ws, 256))
-    return fail(QMOE_ERR_WORKSPACE, "moe_route_decode: workspace %zu < %zu (or misaligned)",
-                ws_bytes, need);
+    return fail(QMOE_ERR_WORKSPACE, "%s: workspace %zu < %zu (or misaligned)", who, ws_bytes,
+                need);
   uint8_t* w = (uint8_t*)ws;
   RouteDecodeParams D{};
   D.r = RouteParams{x, x_dtype, T, H, Wr, bias, E, k, n_shared, ids, p, logits, nullptr, 0, 0};
@@ -321,6 +333,11 @@ int moe_route_decode(const void* x, int x_dtype, int T, int H, const float* Wr,
   const dim3 grid((E + kGemvExperts - 1) / kGemvExperts, D.r.KS);
   const size_t lds = (size_t)kDecodeLdsInts * 4;
   hipStream_t s = (hipStream_t)stream;
+  if (clear_ctr) {
+    const int st = QMOE_LAUNCH("zero_words", zero_words_kernel, dim3(1), 64, 0, s, D.ctr,
+                               (int)(kDecodeCtrBytes / 4));
+    if (st) return st;
+  }
   const int per = (E + 63) / 64;
 #define QMOE_ROUTE_DECODE(PERV) \
   return QMOE_LAUNCH("route_decode", route_decode_kernel<PERV>, grid, kGemvBlock, lds, s, D)
@@ -331,5 +348,83 @@ int moe_route_decode(const void* x, int x_dtype, int T, int H, const float* Wr,
 #undef QMOE_ROUTE_DECODE
 }
 
-}  // extern "C"
+// ------------------------------------------- no-allocation variant ------
+// The workspace of moe_route_decode_noalloc: a file-scope device array, one
+// copy per GPU, held until the process ends.  Host code never passes its
+// name to a kernel (on the host it is only a stand-in symbol): the device
+// address is looked up once per device with hipGetSymbolAddress and kept.
+constexpr size_t kRouteScratchBytes = (size_t)1 << 20;  // 1 MiB
+static __device__ __align__(256) uint8_t scratch[kRouteScratchBytes];
 
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+static bool g_scratch_cleared[kMaxDevices];
+
+// Device address of this device's scratch, looked up with the device current
+// on the first call on it; *cleared says whether a call has already zeroed
+// its counter.
+static int scratch_of_device(int* dev_out, void** out, bool* cleared) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(QMOE_ERR_HIP, "moe_route_decode_noalloc: no current device");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(QMOE_ERR_HIP, "moe_route_decode_noalloc: hipGetSymbolAddress: %s",
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *dev_out = dev;
+  *out = g_scratch_ptr[dev];
+  *cleared = g_scratch_cleared[dev];
+  return QMOE_OK;
+}
+
+static void scratch_mark_cleared(int dev) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  g_scratch_cleared[dev] = true;
+}
+
+}  // namespace qmoe
+
+extern "C" {
+
+int moe_route_decode(const void* x, int x_dtype, int T, int H, const float* Wr,
+                     const float* bias, int E, int k, int n_shared, int32_t* ids, float* p,
+                     float* logits, int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* ws,
+                     size_t ws_bytes, void* stream) {
+  return route_decode_impl("moe_route_decode", x, x_dtype, T, H, Wr, bias, E, k, n_shared, ids,
+                           p, logits, offsets, perm, inv_perm, ws, ws_bytes, false, stream);
+}
+
+size_t moe_route_decode_noalloc_max_bytes(void) { return kRouteScratchBytes; }
+
+int moe_route_decode_noalloc(const void* x, int x_dtype, int T, int H, const float* Wr,
+                             const float* bias, int E, int k, int n_shared, int32_t* ids,
+                             float* p, float* logits, int32_t* offsets, int32_t* perm,
+                             int32_t* inv_perm, void* stream) {
+  const size_t need = moe_route_decode_workspace_size(T, H, E);
+  if (need > kRouteScratchBytes)
+    return fail(QMOE_ERR_UNSUPPORTED,
+                "moe_route_decode_noalloc: T=%d H=%d E=%d needs %zu bytes of scratch, more "
+                "than the %zu it holds",
+                T, H, E, need, kRouteScratchBytes);
+  void* ws = nullptr;
+  bool cleared = false;
+  int dev = 0;
+  int st = scratch_of_device(&dev, &ws, &cleared);
+  if (st) return st;
+  // the counter starts at zero: the array is zero when the code object
+  // loads, the first successful call on a device clears it once more with a
+  // kernel (no memset), and every call leaves it at zero
+  st = route_decode_impl("moe_route_decode_noalloc", x, x_dtype, T, H, Wr, bias, E, k,
+                         n_shared, ids, p, logits, offsets, perm, inv_perm, ws,
+                         kRouteScratchBytes, !cleared, stream);
+  if (st == QMOE_OK && !cleared && T > 0) scratch_mark_cleared(dev);
+  return st;
+}
+
+}  // extern "C"

@@ -54,6 +54,9 @@ _SIGNATURES = {
     "moe_route_decode_workspace_size": (_SZ, [_I, _I, _I]),
     "moe_route_decode": (_I, [_VP, _I, _I, _I, _VP, _VP, _I, _I, _I, _VP, _VP, _VP, _VP, _VP,
                               _VP, _VP, _SZ, _VP]),
+    "moe_route_decode_noalloc_max_bytes": (_SZ, []),
+    "moe_route_decode_noalloc": (_I, [_VP, _I, _I, _I, _VP, _VP, _I, _I, _I, _VP, _VP, _VP, _VP,
+                                      _VP, _VP, _VP]),
     "moe_ffn_workspace_size": (_SZ, [_I, _I, _I]),
     "moe_ffn_tiered": (_I, [ctypes.POINTER(Tier), _I, _I, _I, _I, _VP, _I, _I, _I, _VP, _VP,
                             _VP, _VP, _SZ, _VP]),
@@ -279,6 +282,34 @@ def route_decode(x, Wr, bias, k, n_shared=0, logits=False, ws=None):
                                   _p(ws), ws.numel(), _stream()), "moe_route_decode")
     out = (ids, p, offsets, perm, inv)
     return out + (lg,) if logits else out
+
+
+def route_decode_noalloc(x, Wr, bias, k, n_shared=0, logits=False, out=None):
+    """moe_route_decode_noalloc: as route_decode, with the library's own
+    device scratch instead of a workspace (the call allocates nothing; the
+    output tensors are allocated here unless `out` = (ids, p, offsets, perm,
+    inv_perm[, logits]) is given)."""
+    torch = _torch()
+    _cuda_contig(x, Wr, bias)
+    T, H = x.shape
+    E = Wr.shape[0]
+    kt = k + n_shared
+    dev = x.device
+    if out is None:
+        out = (torch.empty((T, kt), dtype=torch.int32, device=dev),
+               torch.empty((T, kt), dtype=torch.float32, device=dev),
+               torch.empty(E + n_shared + 1, dtype=torch.int32, device=dev),
+               torch.empty(max(T * kt, 1), dtype=torch.int32, device=dev),
+               torch.empty(max(T * kt, 1), dtype=torch.int32, device=dev))
+        if logits:
+            out = out + (torch.empty((T, E), dtype=torch.float32, device=dev),)
+    ids, p, offsets, perm, inv = out[:5]
+    lg = out[5] if len(out) > 5 else None
+    _check(lib().moe_route_decode_noalloc(_p(x), _dtype_code(x), T, H, _p(Wr), _p(bias), E, k,
+                                          n_shared, _p(ids), _p(p), _p(lg), _p(offsets),
+                                          _p(perm), _p(inv), _stream()),
+           "moe_route_decode_noalloc")
+    return out
 
 
 def permute(ids, E, out=None):

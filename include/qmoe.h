@@ -227,6 +227,26 @@ int moe_route_decode(const void *x, int x_dtype, int T, int H, const float *Wr,
                      float *p, float *logits, int32_t *offsets, int32_t *perm,
                      int32_t *inv_perm, void *ws, size_t ws_bytes, void *stream);
 
+/* moe_route_decode_noalloc: moe_route_decode without a caller workspace,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation).  Same
+ * arguments and outputs as moe_route_decode, bit for bit, minus ws and
+ * ws_bytes: the split-K partials and the block counter live in a
+ * library-owned device array of moe_route_decode_noalloc_max_bytes() bytes
+ * (1 MiB) per GPU, held until the process ends.  The call allocates nothing
+ * (no hipMalloc, no memset); the first successful call on a GPU clears the
+ * counter with one small kernel, and every call leaves it at zero.  All calls
+ * on one GPU share that array: calls that overlap on one GPU (other streams,
+ * other threads) race and must not be issued.
+ * Errors: as moe_route_decode; UNSUPPORTED when
+ * moe_route_decode_workspace_size(T, H, E) exceeds the array.               */
+size_t moe_route_decode_noalloc_max_bytes(void);
+int moe_route_decode_noalloc(const void *x, int x_dtype, int T, int H,
+                             const float *Wr, const float *bias, int E, int k,
+                             int n_shared, int32_t *ids, float *p, float *logits,
+                             int32_t *offsets, int32_t *perm, int32_t *inv_perm,
+                             void *stream);
+
 /* moe_permute: stable counting sort of the flat assignments a = t*k + i by
  * expert id ([P2] "优化策略三" groups a layer's routed tokens by expert; bug
  * item 1 shows grouping must survive duplicate ids).
