@@ -544,6 +544,62 @@ def int8_gemv(torch, calls=50):
     return out
 
 
+def int8_prefill(torch, calls=10):
+    """Prefill of the Llama-3-8B layer's seven matrices in Q8_0 at 2048 rows
+    on the int8 matrix cores (qquantize_act_q8 once per input, then
+    qgemm_q8_0_i8 per matrix), beside the 16-bit path a BF16/FP16 prefill
+    takes: the same weights dequantized to fp16 and torch.matmul (the
+    library GEMM)."""
+    from decode_moe_mul_amd import configs, qmoe, synth
+    R = 2048
+    mats = [(n, N, K) for (n, N, K, _) in configs.LLAMA8B_GEMV.mats]
+    bufs, w16 = [], []
+    for i, (n, N, K) in enumerate(mats):
+        W = synth.normal_device((N, K), 0.02, 9, synth.GATE, i, "cuda")
+        bufs.append(qmoe.quantize("q8_0", W))
+        w16.append(qmoe.dequantize("q8_0", bufs[-1], N, K).half())
+        del W
+    xs = {K: torch.from_numpy(synth.normal((R, K), 1.0, 4, synth.ACT, K)).cuda()
+          for K in {K for _, _, K in mats}}
+    x16 = {K: x.half() for K, x in xs.items()}
+    ys = [torch.empty((R, N), dtype=torch.float32, device="cuda") for _, N, _ in mats]
+    flops = sum(2.0 * R * N * K for _, N, K in mats)
+
+    def i8_call(i):
+        qs = {K: qmoe.quantize_act_q8(x) for K, x in xs.items()}
+        for j, (n, N, K) in enumerate(mats):
+            q, d = qs[K]
+            qmoe.gemm_q8_0_i8(bufs[j], N, K, q, d, out=ys[j])
+
+    def f16_call(i):
+        for j, (n, N, K) in enumerate(mats):
+            torch.matmul(x16[K], w16[j].t())
+
+    i8_call(0), f16_call(0)
+    ims = _events_ms(torch, i8_call, calls)
+    fms = _events_ms(torch, f16_call, calls)
+    qmoe.profile_reset()
+    qmoe.profile_enable(True)
+    _events_ms(torch, i8_call, calls)
+    qmoe.profile_enable(False)
+    gemm_ms = qmoe.profile_read("q8_0_i8_gemm")[1] / calls
+    quant_ms = qmoe.profile_read("quantize_act_q8")[1] / calls
+    out = {"workload": "llama3_8b_layer in Q8_0, 2048 rows (7 matrices)",
+           "rows": R, "gflop": round(flops / 1e9, 1),
+           "int8_ms": round(ims, 4), "int8_tokens_per_s": round(R / (ims * 1e-3), 1),
+           "int8_gemm_kernel_ms": round(gemm_ms, 4), "int8_quantize_ms": round(quant_ms, 4),
+           "int8_tops": round(flops / (gemm_ms * 1e-3) / 1e12, 1),
+           "int8_frac_of_int8_peak": round(flops / (gemm_ms * 1e-3) / 5.0e15, 4),
+           "fp16_library_ms": round(fms, 4),
+           "fp16_tflops": round(flops / (fms * 1e-3) / 1e12, 1),
+           "fp16_frac_of_fp16_peak": round(flops / (fms * 1e-3) / 2.5e15, 4),
+           "speedup_int8_over_fp16": round(fms / ims, 3)}
+    del bufs, w16
+    torch.cuda.empty_cache()
+    log(f"int8 prefill: {out}")
+    return out
+
+
 def mx_gemm(torch, calls=20):
     """MXFP4 weights x MXFP8 activations on the block-scaled matrix cores
     (qgemm_mxfp4_mxfp8) for 2048 activation rows: the tail tier's expert
@@ -867,6 +923,7 @@ def main():
     prefill = None if a.decode_only else prefill_chunk(torch)
     mx = None if a.decode_only else mx_gemm(torch)
     i8 = None if a.decode_only else int8_gemv(torch)
+    i8p = None if a.decode_only else int8_prefill(torch)
 
     t = stored_traffic()
     traffic = None if t is None else int(t["traffic_bytes_per_launch"])
@@ -920,6 +977,8 @@ def main():
         out["mx_gemm"] = mx
     if i8 is not None:
         out["int8_gemv"] = i8
+    if i8p is not None:
+        out["int8_prefill"] = i8p
     if not a.no_cpu_baseline:
         log("timing the CPU oracle on bounded samples ...")
         out["cpu_baseline"] = cpu_baseline()

@@ -70,6 +70,7 @@ _SIGNATURES = {
     "qquantize_act_q8": (_I, [_VP, _I, _I, _I, _VP, _VP, _VP]),
     "qgemv_q8_0_i8": (_I, [_VP, _I, _I, _VP, _VP, _I, _VP, _VP]),
     "qgemm_mxfp4_mxfp8": (_I, [_VP, _I, _I, _VP, _VP, _I, _VP, _VP]),
+    "qgemm_q8_0_i8": (_I, [_VP, _I, _I, _VP, _VP, _I, _VP, _VP]),
     "moe_layer_decode_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "moe_layer_decode": (_I, [ctypes.POINTER(Tier), _I, _I, _I, _I, _VP, _I, _I, _VP, _VP, _I,
                               _I, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
@@ -430,6 +431,19 @@ def gemv_q8_0_i8(W, N, K, q, d, out=None):
         out = torch.empty((R, N), dtype=torch.float32, device=q.device)
     _check(lib().qgemv_q8_0_i8(_p(W), N, K, _p(q), _p(d), R, _p(out), _stream()),
            "qgemv_q8_0_i8")
+    return out
+
+
+def gemm_q8_0_i8(W, N, K, q, d, out=None):
+    """y [R, N] = Q8_0 W [N, K] times the int8 activations (q, d) on the
+    int8 matrix cores (prefill-sized R)."""
+    torch = _torch()
+    _cuda_contig(W, q, d)
+    R = q.shape[0]
+    if out is None:
+        out = torch.empty((R, N), dtype=torch.float32, device=q.device)
+    _check(lib().qgemm_q8_0_i8(_p(W), N, K, _p(q), _p(d), R, _p(out), _stream()),
+           "qgemm_q8_0_i8")
     return out
 
 

@@ -369,6 +369,18 @@ int qquantize_act_q8(const void *x, int x_dtype, int R, int K, int8_t *q,
 int qgemv_q8_0_i8(const void *W, int N, int K, const int8_t *q, const float *d,
                   int R, float *y, void *stream);
 
+/* qgemm_q8_0_i8: the same product for prefill-sized R on the int8 matrix
+ * cores ([P1] "NInfer 80 SM port", its int8 artifact: prefill on the int8
+ * tensor cores with int8 activations, section 九 items 2-3):
+ *   y [R, N] fp32 = sum_b (d_w[n, b] d[r, b]) * sum_{k in b} q_w q
+ * with each block's integer sum exact (one v_mfma_i32_16x16x32_i8 per 16 x 16
+ * tile and 32-value block) and the scaling and the sum over blocks in fp32.
+ * W Q8_0 [N, K] (256-byte aligned), q [R, K] int8 (16-byte aligned), d
+ * [R, K/32] fp32 as qquantize_act_q8 writes them.  K % 32 == 0; N*K and R*K
+ * < 2^32.  Any R >= 0 (rows are tiled by 128).                            */
+int qgemm_q8_0_i8(const void *W, int N, int K, const int8_t *q, const float *d,
+                  int R, float *y, void *stream);
+
 /* moe_layer_decode: the whole routed-expert layer of a decode step in one
  * launch ([P2] "瓶颈分析": router top-k over the experts, the selected
  * experts' SwiGLU FFNs, their weighted sum; "优化策略二/三": tiers of mixed

@@ -76,3 +76,54 @@ def test_int8_activation_error_against_fp_activations():
     w = fm.dequantize("q8_0", buf, N, K)
     rel = np.abs(y - x.astype(np.float64) @ w.T) / (np.abs(x) @ np.abs(w).T)
     assert rel.max() < 2e-2 and np.median(rel) < 2e-3
+
+
+# ------------------------------------ int8 matrix cores (prefill rows) ----
+
+@pytest.mark.parametrize("N,K,R", [(16, 32, 1), (70, 96, 33), (130, 384, 130), (257, 1024, 300)])
+def test_gemm_exact_grid_bitexact(N, K, R):
+    """qgemm_q8_0_i8 on the exact grid (weight and activation scales 1,
+    integer codes): every block sum and every partial sum over blocks is an
+    integer far below 2^24, so the result is exact; ragged row and column
+    tiles, an odd block count (K = 96)."""
+    rng = np.random.default_rng(N + K + R)
+    W = rng.integers(-127, 128, (N, K)).astype(np.float64)
+    W[:, ::32] = 127.0
+    buf = fm.quantize("q8_0", W)
+    x = rng.integers(-20, 21, (R, K)).astype(np.float32)
+    x[:, ::32] = 127.0
+    q, d = qmoe.quantize_act_q8(to_gpu(x))
+    y = to_np(qmoe.gemm_q8_0_i8(to_gpu(buf), N, K, q, d))
+    ref, _ = int8.gemv_q8_0_i8(buf, N, K, x)
+    assert_bitexact(y, ref, f"int8 gemm exact grid {N}x{K} R={R}")
+
+
+@pytest.mark.parametrize("N,K,R", [(640, 2048, 2048), (2048, 640, 300), (4096, 14336, 200),
+                                   (14336, 4096, 2048), (130, 384, 17)])
+def test_gemm_within_bound(N, K, R):
+    """Realistic Q8_0 weights and activations at prefill row counts; up to 64
+    sampled output columns of the large shapes (rows of W quantize
+    independently, so a subset of rows is the same tensor's rows)."""
+    Wd = synth.normal_device((N, K), 0.02, 11, synth.GATE, N, "cuda")
+    buf = qmoe.quantize("q8_0", Wd)
+    x = synth.normal((R, K), 1.0, 12, synth.ACT, R)
+    q, d = qmoe.quantize_act_q8(to_gpu(x))
+    y = to_np(qmoe.gemm_q8_0_i8(buf, N, K, q, d))
+    cols = np.arange(N) if N <= 130 else np.sort(
+        np.random.default_rng(N).choice(N, 64, replace=False))
+    Wc = to_np(Wd[torch.from_numpy(cols).cuda()])
+    ref, bound = int8.gemv_q8_0_i8(fm.quantize("q8_0", Wc), len(cols), K, x)
+    assert_within_bound(y[:, cols], ref, bound, what=f"int8 gemm {N}x{K} R={R}")
+
+
+def test_gemm_equals_gemv_on_few_rows():
+    """The matrix-core GEMM and the v_dot4 GEMV take the same integer block
+    sums; their fp32 sums over blocks differ at most by rounding order."""
+    N, K, R = 512, 2048, 16
+    buf = fm.quantize("q8_0", synth.normal((N, K), 0.02, 13, synth.UP, 0))
+    x = synth.normal((R, K), 1.0, 14, synth.ACT, 2)
+    q, d = qmoe.quantize_act_q8(to_gpu(x))
+    a = to_np(qmoe.gemm_q8_0_i8(to_gpu(buf), N, K, q, d))
+    b = to_np(qmoe.gemv_q8_0_i8(to_gpu(buf), N, K, q, d))
+    _, bound = int8.gemv_q8_0_i8(buf, N, K, x)
+    assert np.all(np.abs(a - b) <= 1e-5 * bound)
