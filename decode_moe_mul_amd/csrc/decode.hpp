@@ -695,6 +695,7 @@ struct FfnParams {
   int ntiles, G, tile_rows;
   int m_max;       // experts with more rows use the matrix cores
   int ntiles_big;  // blocks (column tiles) per such expert
+  int chunk;       // rows staged per dot-product pass (0: the kernel's RC)
 };
 
 // The tier holding expert e, assembled field by field with constant indices
@@ -776,15 +777,30 @@ QMOE_D int scheduled_expert(const int* offs, int E, int m_max, int b, int ntiles
   return red[2 * kWaves];
 }
 
+// Weight rows [rb, re) of the phase's matrix that work item (e, tile) covers
+// (empty when rb >= re): few-row experts take row tiles of tile_rows, many-row
+// experts slices of whole matrix-core passes, N split over at most
+// ntiles_big blocks.
+template <int PHASE>
+QMOE_D void item_rows(const FfnParams& P, int tile, bool big, int& rb, int& re) {
+  const int N = PHASE == 0 ? P.F : P.H;
+  const int pass = 16 * mfma_cols_per_pass(PHASE == 0 ? 2 : 1);
+  const int cpt = ((N + P.ntiles_big - 1) / P.ntiles_big + pass - 1) / pass * pass;
+  rb = big ? tile * cpt : tile * P.tile_rows;
+  re = min(N, rb + (big ? cpt : P.tile_rows));
+}
+
 // One work item of the routed FFN: row tile `tile` of expert e, whose rows
 // are positions pos0 .. pos0 + m - 1 of the permutation (perm_of(pos) gives
 // the flat assignment t * k + i).  PHASE 0: gate/up + SwiGLU -> h;
-// PHASE 1: down -> o.  COH: h and o are handed to other blocks of the same
-// launch, so they are written through and h is read past the L2.
-template <int PHASE, int RC, bool MFMA, bool COH, class PermOf>
+// PHASE 1: down -> o.  COH: h is read past the L2 (written by other blocks
+// of the same launch); COH_OUT: h and o are written through for readers in
+// the same launch.
+template <int PHASE, int RC, bool MFMA, bool COH, bool COH_OUT, class PermOf>
 QMOE_D void ffn_item(const FfnParams& P, int e, int tile, bool big, int pos0, int m,
                      uint8_t* smem, PermOf perm_of) {
-  const int H = P.H, F = P.F, kk = P.k, dtype = P.x_dtype, G = P.G, tile_rows = P.tile_rows;
+  const int H = P.H, F = P.F, kk = P.k, dtype = P.x_dtype, G = P.G;
+  const int chunk = P.chunk > 0 && P.chunk < RC ? P.chunk : RC;
   const char* xb = (const char*)P.x;
   float* hbuf = P.h;
   float* obuf = P.o;
@@ -792,13 +808,8 @@ QMOE_D void ffn_item(const FfnParams& P, int e, int tile, bool big, int pos0, in
   if (!tier_of(P.tiers, P.n_tiers, e, t)) return;
   const int fmt = PHASE == 0 ? t.fmt_gate_up : t.fmt_down;
   const int N = PHASE == 0 ? F : H, K = PHASE == 0 ? H : F;
-  // few-row experts: weight rows [rb, re) of a row tile; many-row experts:
-  // a slice of whole matrix-core passes, N split over at most
-  // ntiles_big blocks
-  const int pass = 16 * mfma_cols_per_pass(PHASE == 0 ? 2 : 1);
-  const int cpt = ((N + P.ntiles_big - 1) / P.ntiles_big + pass - 1) / pass * pass;
-  const int rb = big ? tile * cpt : tile * tile_rows;
-  const int re = min(N, rb + (big ? cpt : tile_rows));
+  int rb, re;
+  item_rows<PHASE>(P, tile, big, rb, re);
   if (rb >= re) return;
   const size_t xrow_bytes = (size_t)H * (dtype == QMOE_F32 ? 4 : 2);
   auto x_row = [=](int rr) {
@@ -806,13 +817,13 @@ QMOE_D void ffn_item(const FfnParams& P, int e, int tile, bool big, int pos0, in
   };
   auto h_out = [=](int n, int rr, const float* a) {
     float* dst = hbuf + (size_t)(pos0 + rr) * F + n;
-    if constexpr (COH) store_coherent(dst, silu_mul(a[0], a[1]));
+    if constexpr (COH_OUT) store_coherent(dst, silu_mul(a[0], a[1]));
     else *dst = silu_mul(a[0], a[1]);
   };
   auto h_row = [=](int rr) { return (const void*)(hbuf + (size_t)(pos0 + rr) * F); };
   auto o_out = [=](int n, int rr, const float* a) {
     float* dst = obuf + (size_t)(pos0 + rr) * H + n;
-    if constexpr (COH) store_coherent(dst, a[0]);
+    if constexpr (COH_OUT) store_coherent(dst, a[0]);
     else *dst = a[0];
   };
 #define QMOE_FFN_CASE(FM)                                                                  \
@@ -825,13 +836,14 @@ QMOE_D void ffn_item(const FfnParams& P, int e, int tile, bool big, int pos0, in
         mfma_cols<FM, 2, QMOE_F32>(mats, K, rb, re, m, smem, x_row, h_out);                \
       else if (MFMA && big)                                                                \
         mfma_cols<FM, 2, QMOE_BF16>(mats, K, rb, re, m, smem, x_row, h_out);               \
-      else valu_rows<FM, 2, RC>(mats, K, rb, re, G, m, dtype, smem, x_row, h_out);         \
+      else valu_rows<FM, 2, RC>(mats, K, rb, re, G, m, dtype, smem, x_row, h_out, chunk);  \
     } else {                                                                               \
       const Mat mats[1] = {mat_of((const uint8_t*)t.down + eo, FM, N, K)};                 \
       if (MFMA && big)                                                                     \
         mfma_cols<FM, 1, COH ? kF32Coherent : QMOE_F32>(mats, K, rb, re, m, smem, h_row,   \
                                                         o_out);                            \
-      else valu_rows<FM, 1, RC, COH>(mats, K, rb, re, G, m, QMOE_F32, smem, h_row, o_out); \
+      else valu_rows<FM, 1, RC, COH>(mats, K, rb, re, G, m, QMOE_F32, smem, h_row, o_out,  \
+                                     chunk);                                               \
     }                                                                                      \
   } break;
   switch (fmt) {

@@ -148,8 +148,8 @@ __global__ __launch_bounds__(kBlock, (PHASE == 1 || RC <= 2) ? 3 : 2) void ffn_d
   big = __builtin_amdgcn_readfirstlane((int)big) != 0;
   const int pos0 = __builtin_amdgcn_readfirstlane(offs[e]);
   const int m = __builtin_amdgcn_readfirstlane(offs[e + 1]) - pos0;
-  ffn_item<PHASE, RC, MFMA, false>(P, e, tile, big, pos0, m, smem,
-                                   [=](int i) { return perm[i]; });
+  ffn_item<PHASE, RC, MFMA, false, false>(P, e, tile, big, pos0, m, smem,
+                                          [=](int i) { return perm[i]; });
 }
 
 // ------------------------------------------------------ host helpers ----
@@ -325,6 +325,28 @@ static int ffn_dispatch(const FfnParams& P, int RC, dim3 grid, size_t lds, hipSt
 
 int validate_tiers(const qmoe_tier* tiers, int n_tiers, int E, int H, int F, bool prefill);
 
+// Blocks per CU for one phase of the routed FFN: 8 per 256 KB of weights a
+// block would stream at 8 per CU (ranks experts of the phase's largest tier),
+// between 4 and 24.  Long blocks leave a long tail once the last ones start
+// (16 rows through 256 experts of [2048, 7168] Q4_K, about 2 MB per block at
+// 8 per CU; 8 / 12 / 16 / 24 / 32 / 48 per CU: gate/up 376 / 367 / 365 / 354
+// / 355 / 367 us per step of the three decode calls); a few rows through
+// small experts (about 60 KB per block at 8) run faster as fewer, longer
+// blocks (the 6-row tiered call 79.4 -> 75.1 us at 4 per CU).
+int ffn_blocks_per_cu(const qmoe_tier* tiers, int n_tiers, int H, int F, int phase,
+                      int ranks) {
+  size_t worst = 0;
+  for (int i = 0; i < n_tiers; ++i) {
+    const size_t b = phase == 0 ? 2 * layout_of(tiers[i].fmt_gate_up, F, H).total
+                                : layout_of(tiers[i].fmt_down, H, F).total;
+    worst = std::max(worst, b);
+  }
+  int cus = cu_count();
+  if (cus <= 0) cus = 256;
+  const double per_block = (double)ranks * (double)worst / (8.0 * cus);
+  return std::min(24, std::max(4, (int)(8.0 * per_block / (double)(256 << 10))));
+}
+
 // LDS budget for staged activation rows in the routed FFN.  Registers, not
 // LDS, bound the resident blocks of these kernels (2-3 per CU), so a block
 // may take up to the 64 KB a launch can request.
@@ -359,28 +381,6 @@ int qgemv_batch(const qmoe_gemv_desc* descs, int n, void* stream) {
 size_t moe_ffn_workspace_size(int T, int k, int F) {
   if (T < 0 || k < 0 || F < 0) return 0;
   return round_up256((size_t)T * k * F * sizeof(float)) + 256;
-}
-
-// Blocks per CU for one phase of the routed FFN: 8 per 256 KB of weights a
-// block would stream at 8 per CU (ranks experts of the phase's largest tier),
-// between 4 and 24.  Long blocks leave a long tail once the last ones start
-// (16 rows through 256 experts of [2048, 7168] Q4_K, about 2 MB per block at
-// 8 per CU; 8 / 12 / 16 / 24 / 32 / 48 per CU: gate/up 376 / 367 / 365 / 354
-// / 355 / 367 us per step of the three decode calls); a few rows through
-// small experts (about 60 KB per block at 8) run faster as fewer, longer
-// blocks (the 6-row tiered call 79.4 -> 75.1 us at 4 per CU).
-static int ffn_blocks_per_cu(const qmoe_tier* tiers, int n_tiers, int H, int F, int phase,
-                             int ranks) {
-  size_t worst = 0;
-  for (int i = 0; i < n_tiers; ++i) {
-    const size_t b = phase == 0 ? 2 * layout_of(tiers[i].fmt_gate_up, F, H).total
-                                : layout_of(tiers[i].fmt_down, H, F).total;
-    worst = std::max(worst, b);
-  }
-  int cus = cu_count();
-  if (cus <= 0) cus = 256;
-  const double per_block = (double)ranks * (double)worst / (8.0 * cus);
-  return std::min(24, std::max(4, (int)(8.0 * per_block / (double)(256 << 10))));
 }
 
 int moe_ffn_tiered(const qmoe_tier* tiers, int n_tiers, int E, int H, int F, const void* x,

@@ -106,6 +106,41 @@ QMOE_D void permute_block(const int32_t* ids, int A, int E, int W, int nbits, in
   for (long long i = (long long)total + threadIdx.x; i < A; i += NT) perm[i] = -1;
 }
 
+// The same stable counting sort for the few assignments of decode rows (A
+// <= NT, ids in LDS), with one block-wide barrier instead of the histogram
+// passes: offsets[e] = number of valid ids below e (thread e counts them);
+// assignment a goes to offsets[ids[a]] plus the number of earlier
+// assignments with the same id.  The result is the unique stable order, so
+// it equals permute_block's.  offs holds E + 1 ints of LDS.
+template <int NT>
+QMOE_D void permute_small(const int32_t* ids, int A, int E, int32_t* offsets, int32_t* perm,
+                          int32_t* inv, int* offs) {
+  for (int e = threadIdx.x; e <= E; e += NT) {
+    int c = 0;
+    for (int b = 0; b < A; ++b) {
+      const int id = ids[b];
+      c += id >= 0 && id < e;
+    }
+    offs[e] = c;
+    offsets[e] = c;
+  }
+  __syncthreads();
+  const int total = offs[E];
+  for (int a = threadIdx.x; a < A; a += NT) {
+    const int id = ids[a];
+    if (id >= 0 && id < E) {
+      int r = 0;
+      for (int b = 0; b < a; ++b) r += ids[b] == id;
+      const int pos = offs[id] + r;
+      perm[pos] = (int32_t)a;
+      inv[a] = pos;
+    } else {
+      inv[a] = -1;
+    }
+  }
+  for (int i = total + threadIdx.x; i < A; i += NT) perm[i] = -1;
+}
+
 // waves of a permute_block over A assignments and E experts with `lds_ints`
 // ints of LDS for hist: one per 64 assignments (more would only add empty
 // histograms to clear and scan), at most max_waves and what the LDS holds

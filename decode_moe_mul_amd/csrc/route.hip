@@ -205,8 +205,11 @@ __global__ __launch_bounds__(kGemvBlock) void route_decode_kernel(RouteDecodePar
   }
   __syncthreads();
   int* hist = (int*)smem + ((A + 63) & ~63);
-  permute_block<kGemvBlock>(ids_l, A, D.E_total, D.W, D.nbits, D.offsets, D.perm, D.inv, hist,
-                             hist + D.W * D.E_total);
+  if (A <= kGemvBlock)
+    permute_small<kGemvBlock>(ids_l, A, D.E_total, D.offsets, D.perm, D.inv, hist);
+  else
+    permute_block<kGemvBlock>(ids_l, A, D.E_total, D.W, D.nbits, D.offsets, D.perm, D.inv,
+                               hist, hist + D.W * D.E_total);
   if (threadIdx.x == 0)
     __hip_atomic_store(&D.ctr[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

@@ -94,6 +94,36 @@ QMOE_D float wave_sum16(float (&acc)[kGemvRowsMax]) {
   return v;
 }
 
+// The weight-row half of router_partials: wave w's expert row over the slice,
+// 4 float4 per lane (zero past the slice).
+template <int NT>
+QMOE_D void router_wrow(const RouteParams& P, int b, int ks, float4 (&w)[4]) {
+  const int k0 = ks * P.ks_len;
+  const int len = min(P.ks_len, P.H - k0);
+  const int lane = threadIdx.x & 63;
+  const int e = b * (NT / 64) + (threadIdx.x >> 6);
+  const float* wrow = P.Wr + (size_t)min(e, P.E - 1) * P.H + k0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int j = 4 * lane + 256 * u;
+    w[u] = j < len ? *(const float4*)(wrow + j) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+}
+
+template <int NT>
+QMOE_D void router_stage(const RouteParams& P, float* xsl, int ks) {
+  const int k0 = ks * P.ks_len;
+  const int len = min(P.ks_len, P.H - k0);
+  if (P.x_dtype == QMOE_F32)
+    stage_x_slice<QMOE_F32, NT>(P, k0, len, xsl);
+  else
+    stage_x_slice<QMOE_BF16, NT>(P, k0, len, xsl);
+}
+
+template <bool COH, int NT>
+QMOE_D void router_dots(const RouteParams& P, const float* xsl, int b, int ks,
+                        const float4 (&w)[4]);
+
 // Block (b, ks) of the split-K router, NT threads: wave w handles expert
 // (NT/64) b + w over values
 // [ks*ks_len, (ks+1)*ks_len) of the hidden dimension (ks_len <= 1024, a
@@ -103,23 +133,23 @@ QMOE_D float wave_sum16(float (&acc)[kGemvRowsMax]) {
 // returns (no early exit), so callers may synchronise afterwards.
 template <bool COH, int NT>
 QMOE_D void router_partials(const RouteParams& P, float* xsl, int b, int ks) {
+  float4 w[4];
+  router_wrow<NT>(P, b, ks, w);
+  router_stage<NT>(P, xsl, ks);
+  __syncthreads();
+  router_dots<COH, NT>(P, xsl, b, ks, w);
+}
+
+// The dot products of router_partials against the staged slice (every
+// thread returns, so callers may synchronise afterwards).
+template <bool COH, int NT>
+QMOE_D void router_dots(const RouteParams& P, const float* xsl, int b, int ks,
+                        const float4 (&w)[4]) {
   const int k0 = ks * P.ks_len;
   const int len = min(P.ks_len, P.H - k0);
   const int lane = threadIdx.x & 63;
   const int e = b * (NT / 64) + (threadIdx.x >> 6);
   const bool has_e = e < P.E;
-  const float* wrow = P.Wr + (size_t)min(e, P.E - 1) * P.H + k0;
-  float4 w[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int j = 4 * lane + 256 * u;
-    w[u] = j < len ? *(const float4*)(wrow + j) : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-  if (P.x_dtype == QMOE_F32)
-    stage_x_slice<QMOE_F32, NT>(P, k0, len, xsl);
-  else
-    stage_x_slice<QMOE_BF16, NT>(P, k0, len, xsl);
-  __syncthreads();
   float acc[kGemvRowsMax];
 #pragma unroll
   for (int t = 0; t < kGemvRowsMax; ++t) {

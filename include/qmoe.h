@@ -388,26 +388,27 @@ int qgemm_q8_0_i8(const void *W, int N, int K, const int8_t *q, const float *d,
  *   moe_route_decode(x, Wr, bias, E, k, n_shared) -> ids, p, offsets, perm,
  *   inv_perm;  moe_ffn_tiered(tiers, E + n_shared, H, F, x, T, k + n_shared)
  *   -> o;  moe_combine(o, inv_perm, p, T, k + n_shared, H, NULL) -> y
- * computes, with the same arithmetic: the outputs are equal bit for bit
- * whenever both paths pick the same dot-product blocking (always, unless
- * staged rows of length H or F need more than about 60 KB of LDS).  A
- * cooperative grid of co-resident blocks runs the phases separated by three
- * device-wide barriers (a counter in the workspace).
+ * computes, with the same arithmetic: the outputs are equal bit for bit.  One
+ * plain launch holds, in block-index order, the router blocks (the last of
+ * them routes every row and publishes the routing), the gate/up blocks and
+ * the down blocks of moe_ffn_tiered's schedule; each block waits only for the
+ * data it reads (the routing, its expert's h), through counters in the
+ * workspace, and the block that writes the last piece of a (token, 64-row
+ * chunk) of y sums that chunk.  Blocks wait only on blocks of lower index.
  * Arguments: tiers cover ids [0, E + n_shared) (shared experts are ids E..,
  * always selected with weight 1); x [T, H] (x_dtype), Wr [E, H] fp32, bias [E]
  * fp32 or NULL; outputs ids/p [T, k+n_shared], offsets [E+n_shared+1], perm
  * and inv_perm [T*(k+n_shared)], y [T, H] fp32.  x, Wr and y 16-byte aligned.
- * Limits: T <= 16, 1 <= k <= min(E, 64), E <= 512, H % 4 == 0, plus
- * moe_ffn_tiered's (UNSUPPORTED when the routing of T*(k+n_shared) rows and
- * the staged rows do not fit 64 KB of LDS, or the device cannot hold the
- * grid).  T == 0 writes zero offsets and nothing else.
+ * Limits: T <= 16, 1 <= k <= min(E, 64), E <= 512, H % 4 == 0,
+ * T*(k+n_shared) <= 1024 and 768 + 2*(E+n_shared) + T*ceil(H/64) <= 4096
+ * (the counters), plus moe_ffn_tiered's (UNSUPPORTED beyond).  T == 0 writes
+ * zero offsets and nothing else.
  * Workspace: moe_layer_decode_workspace_size(T, H, E, F, k, n_shared) bytes,
- * 256-byte aligned, whose first 12288 bytes (the barrier counters) must be
- * zero before the first call that uses it; every call leaves them zero again.
- * A nonzero first word (uint32 at byte 0) after a call means a barrier wait
- * ran out (about a second) and the outputs are invalid; the workspace must
- * then be zeroed again.  Calls sharing one workspace must not run
- * concurrently. */
+ * 256-byte aligned, whose first 16384 bytes (the counters) must be zero
+ * before the first call that uses it; every call leaves them zero again.
+ * A nonzero first word (uint32 at byte 0) after a call means a wait ran out
+ * (about a second) and the outputs are invalid; the workspace must then be
+ * zeroed again.  Calls sharing one workspace must not run concurrently. */
 size_t moe_layer_decode_workspace_size(int T, int H, int E, int F, int k,
                                        int n_shared);
 int moe_layer_decode(const qmoe_tier *tiers, int n_tiers, int E, int H, int F,

@@ -181,7 +181,7 @@ def test_one_launch_layer_validation(L):
     arr = (qmoe.Tier * 1)(qmoe.Tier(0, 16, 0, 0, 256000, 256000, 256000))
     need = L.moe_layer_decode_workspace_size(4, 64, 16, 64, 2, 0)
     # counter block + split-K partials + h [A, F] + o [A, H], each 256-aligned
-    assert need == 12288 + 256 + 2048 + 2048
+    assert need == 16384 + 256 + 2048 + 2048 + 512   # + schedule table (64 entries)
     args = lambda T, E, k, ns, ws: (arr, 1, E, 64, 64, fake, 0, T, fake, None, k, ns, fake, fake,
                                     fake, fake, fake, fake, fake, ws, None)
     assert L.moe_layer_decode(*args(17, 16, 2, 0, 1 << 30)) == -2      # rows beyond 16

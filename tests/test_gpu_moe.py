@@ -322,9 +322,9 @@ ONE_LAUNCH_CASES = [(configs.TINY, 4), (SMALL_TIERED, 1), (SMALL_TIERED, 5), (SM
 
 
 def _counter_words(ws):
-    """The barrier counters (first 12288 bytes of the workspace): nonzero
+    """The counters (first 16384 bytes of the workspace): nonzero
     words, at most 3 listed; [] when all are zero as every call must leave them."""
-    w = to_np(ws["layer"][:12288].view(torch.int32))
+    w = to_np(ws["layer"][:16384].view(torch.int32))
     return w[w != 0][:3].tolist()
 
 
@@ -381,8 +381,22 @@ def test_one_launch_repeated_calls_reuse_the_counter():
             outs[T] = yv
 
 
-def test_one_launch_limits():
+def test_one_launch_wide_hidden_on_the_matrix_cores():
+    """A 28672-wide hidden row does not fit the LDS staging of the dot-product
+    path; the one-launch layer then runs every gate/up item on the matrix
+    cores, as moe_ffn_tiered does, and equals the separate calls bit for bit."""
     layer = _layer(WIDE_HIDDEN)
-    _, xg = _x(WIDE_HIDDEN, 1)
-    with pytest.raises(RuntimeError, match="do not fit LDS"):
-        layer.forward(xg, one_launch=True)
+    _, xg = _x(WIDE_HIDDEN, 3)
+    y_sep = to_np(layer.forward(xg)[0]).copy()
+    y, ws = layer.forward(xg, one_launch=True)
+    assert_bitexact(to_np(y), y_sep, "wide hidden one launch")
+    assert _counter_words(ws) == []
+
+
+def test_one_launch_limits():
+    cfg = SMALL_TIERED
+    layer = _layer(cfg)
+    _, xg = _x(cfg, 17)
+    with pytest.raises(RuntimeError, match="rows"):
+        qmoe.layer_decode(layer.tier_arrays[0], cfg.E, cfg.H, cfg.F, xg, layer.Wr, layer.bias,
+                          cfg.k)
