@@ -872,12 +872,26 @@ inline size_t stage_bytes(int RC, int K) {
   return (size_t)RC * tok_stride(U) + (size_t)RC * U * sizeof(float2);
 }
 
+// LDS budget for staged activation rows in the routed FFN.  Registers bound
+// the resident blocks of these kernels (2-3 per CU), so a block may stage up
+// to 96 KB of the 160 KB a gfx950 compute unit holds (four rows of a
+// 7168-wide hidden dimension take 68 KB).
+constexpr size_t kFfnStageBudget = 96 << 10;
+
+// Kernels that may take more than 64 KB of LDS declare it (host side).
+template <class Kernel>
+inline void allow_lds(Kernel kernel, size_t lds) {
+  if (lds > (64u << 10))
+    (void)hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)lds);
+}
+
 // Rows per register pass: 1, 2 or 4 (enough for `rows`), halved until the
 // staged rows fit `budget` bytes of LDS.  0 if even one row does not fit.
 inline int pick_rc(int rows, int K, size_t budget = kLdsCap) {
   int rc = rows <= 1 ? 1 : rows <= 2 ? 2 : 4;
   while (rc > 1 && stage_bytes(rc, K) > budget) rc >>= 1;
-  return stage_bytes(rc, K) <= (size_t)kLdsCap ? rc : 0;
+  return stage_bytes(rc, K) <= (budget > (size_t)kLdsCap ? budget : (size_t)kLdsCap) ? rc : 0;
 }
 
 // Rows per block for N rows when `work_items` independent matrices run in

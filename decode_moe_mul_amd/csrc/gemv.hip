@@ -313,7 +313,11 @@ template <int PHASE, bool MFMA>
 static int ffn_dispatch2(const FfnParams& P, int RC, dim3 grid, size_t lds, hipStream_t s) {
   const char* name = PHASE == 0 ? "ffn_gate_up" : "ffn_down";
   if (RC == 1) return QMOE_LAUNCH(name, (ffn_decode_kernel<PHASE, 1, MFMA>), grid, kBlock, lds, s, P);
-  if (RC == 2) return QMOE_LAUNCH(name, (ffn_decode_kernel<PHASE, 2, MFMA>), grid, kBlock, lds, s, P);
+  if (RC == 2) {
+    allow_lds(ffn_decode_kernel<PHASE, 2, MFMA>, lds);
+    return QMOE_LAUNCH(name, (ffn_decode_kernel<PHASE, 2, MFMA>), grid, kBlock, lds, s, P);
+  }
+  allow_lds(ffn_decode_kernel<PHASE, 4, MFMA>, lds);
   return QMOE_LAUNCH(name, (ffn_decode_kernel<PHASE, 4, MFMA>), grid, kBlock, lds, s, P);
 }
 
@@ -347,10 +351,7 @@ int ffn_blocks_per_cu(const qmoe_tier* tiers, int n_tiers, int H, int F, int pha
   return std::min(24, std::max(4, (int)(8.0 * per_block / (double)(256 << 10))));
 }
 
-// LDS budget for staged activation rows in the routed FFN.  Registers, not
-// LDS, bound the resident blocks of these kernels (2-3 per CU), so a block
-// may take up to the 64 KB a launch can request.
-constexpr size_t kFfnStageBudget = kLdsCap;
+
 
 }  // namespace qmoe
 

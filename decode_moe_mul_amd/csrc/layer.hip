@@ -391,6 +391,7 @@ static size_t sched_entries(int T, int H, int E, int F, int k, int n_shared) {
 
 template <int RC, bool MFMA>
 static int layer_launch(const LayerParams& P, unsigned blocks, size_t lds, hipStream_t s) {
+  allow_lds(layer_decode_kernel<RC, MFMA>, lds);
   return QMOE_LAUNCH("layer_decode", (layer_decode_kernel<RC, MFMA>), dim3(blocks), kBlock, lds,
                      s, P);
 }
@@ -447,7 +448,7 @@ int moe_layer_decode(const qmoe_tier* tiers, int n_tiers, int E, int H, int F, c
   int KS, ks_len;
   route_split(T, H, KS, ks_len);
   // the FFN's register blocking exactly as moe_ffn_tiered picks it
-  const int rc1 = pick_rc(T, H), rc2 = pick_rc(T, F);
+  const int rc1 = pick_rc(T, H, kFfnStageBudget), rc2 = pick_rc(T, F, kFfnStageBudget);
   const bool mfma = T > rc1 || T > rc2 || rc1 == 0 || rc2 == 0;
   const int rc_max = std::max(rc1, rc2);
   // LDS: the largest of the roles' needs
@@ -458,7 +459,7 @@ int moe_layer_decode(const qmoe_tier* tiers, int n_tiers, int E, int H, int F, c
   if (rc1) lds = std::max(lds, stage_bytes(rc1, H));
   if (rc2) lds = std::max(lds, stage_bytes(rc2, F));
   if (mfma) lds = std::max(lds, mfma_red_bytes(2));
-  if (lds > (size_t)kLdsCap)
+  if (lds > kFfnStageBudget)
     return fail(QMOE_ERR_UNSUPPORTED, "moe_layer_decode: rows of H=%d / F=%d do not fit LDS", H,
                 F);
 
