@@ -378,7 +378,8 @@ def summarize_prefill_pmc(dirs):
             if "copyBuffer" in k and c in cs:
                 cp.update(cs[c])
         if cp:
-            cal[c] = CAL_BYTES / (cp[max(cp, key=int)] * 1024)   # bytes per counted byte
+            # the calibration copy is the largest plain copy of the run
+            cal[c] = CAL_BYTES / (max(cp.values()) * 1024)   # bytes per counted byte
     counters = sorted({c for k, cs in per.items() for c in cs})
     print("| kernel | launches | " + " | ".join(counters) + " |")
     print("|---|---:|" + "---:|" * len(counters))

@@ -257,38 +257,42 @@ QMOE_D void load32(const void* row, int dtype, int u, float v[32]) {
 //   Q4_0: {1024 S + 8 X, 0}          Q4_K: {1024 S, X}  (X meets the min)
 //   Q6_K: {1024 S + 32 X} over elements 0..15 and over 16..31
 //   Q8_0: {1152 S, 0}                MXFP4: {0, 0}
+template <int FMT>
+QMOE_D void stage_unit(uint8_t* xs, float2* sb, int r, int u, int U, const float (&v)[32]) {
+  uint32_t w[16];
+  float S[2] = {0.f, 0.f}, X[2] = {0.f, 0.f};
+#pragma unroll
+  for (int p = 0; p < 16; ++p) {
+    const bool up4 = pair_up4<FMT>(p);
+    const float sc = up4 ? 0.0625f : 1.f;
+    const float a = f16_bits_to_f32(f32_to_f16_bits(v[pair_elem_biased<FMT>(p, 0)])) * sc;
+    const float b = f16_bits_to_f32(f32_to_f16_bits(v[pair_elem_biased<FMT>(p, 1)])) * sc;
+    w[p] = pack_h2(a, b);
+    const float fa = f16_bits_to_f32(w[p] & 0xFFFFu), fb = f16_bits_to_f32(w[p] >> 16);
+    S[p >> 3] += fa + fb;
+    X[p >> 3] += up4 ? 16.f * (fa + fb) : fa + fb;
+  }
+  float2 out = make_float2(0.f, 0.f);
+  if constexpr (FMT == QMOE_Q4_0) out.x = 1024.f * (S[0] + S[1]) + 8.f * (X[0] + X[1]);
+  if constexpr (FMT == QMOE_Q4_K) out = make_float2(1024.f * (S[0] + S[1]), X[0] + X[1]);
+  if constexpr (FMT == QMOE_Q6_K)
+    out = make_float2(1024.f * S[0] + 32.f * X[0], 1024.f * S[1] + 32.f * X[1]);
+  if constexpr (FMT == QMOE_Q8_0) out.x = 1152.f * (S[0] + S[1]);
+  sb[r * U + u] = out;
+  uint4* dst = (uint4*)(xs + (size_t)r * tok_stride(U) + unit_off(u));
+  dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+  dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  dst[2] = make_uint4(w[8], w[9], w[10], w[11]);
+  dst[3] = make_uint4(w[12], w[13], w[14], w[15]);
+}
+
 template <int FMT, bool COH = false, class Src>
 QMOE_D void stage_rows(uint8_t* xs, float2* sb, int rc, int U, Src src, int dtype) {
-  const int ts = tok_stride(U);
   for (int idx = threadIdx.x; idx < rc * U; idx += kBlock) {
     const int r = idx / U, u = idx - r * U;
     float v[32];
     load32<COH>(src(r), dtype, u, v);
-    uint32_t w[16];
-    float S[2] = {0.f, 0.f}, X[2] = {0.f, 0.f};
-#pragma unroll
-    for (int p = 0; p < 16; ++p) {
-      const bool up4 = pair_up4<FMT>(p);
-      const float sc = up4 ? 0.0625f : 1.f;
-      const float a = f16_bits_to_f32(f32_to_f16_bits(v[pair_elem_biased<FMT>(p, 0)])) * sc;
-      const float b = f16_bits_to_f32(f32_to_f16_bits(v[pair_elem_biased<FMT>(p, 1)])) * sc;
-      w[p] = pack_h2(a, b);
-      const float fa = f16_bits_to_f32(w[p] & 0xFFFFu), fb = f16_bits_to_f32(w[p] >> 16);
-      S[p >> 3] += fa + fb;
-      X[p >> 3] += up4 ? 16.f * (fa + fb) : fa + fb;
-    }
-    float2 out = make_float2(0.f, 0.f);
-    if constexpr (FMT == QMOE_Q4_0) out.x = 1024.f * (S[0] + S[1]) + 8.f * (X[0] + X[1]);
-    if constexpr (FMT == QMOE_Q4_K) out = make_float2(1024.f * (S[0] + S[1]), X[0] + X[1]);
-    if constexpr (FMT == QMOE_Q6_K)
-      out = make_float2(1024.f * S[0] + 32.f * X[0], 1024.f * S[1] + 32.f * X[1]);
-    if constexpr (FMT == QMOE_Q8_0) out.x = 1152.f * (S[0] + S[1]);
-    sb[idx] = out;
-    uint4* dst = (uint4*)(xs + (size_t)r * ts + unit_off(u));
-    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
-    dst[2] = make_uint4(w[8], w[9], w[10], w[11]);
-    dst[3] = make_uint4(w[12], w[13], w[14], w[15]);
+    stage_unit<FMT>(xs, sb, r, u, U, v);
   }
 }
 
@@ -312,32 +316,78 @@ QMOE_D float group_reduce(float v, int G) {
 }
 
 // ---------------------------------------------- few rows: fp16 dots -----
-// Rows [rb, re) of NMAT matrices [*, K] against the rc (<= RC) staged rows.
-// sink(row, r, const float* v[NMAT]) is called once per (row, r).
-template <int FMT, int NMAT, int RC, class Sink>
-QMOE_D void valu_pass(const Mat (&mats)[NMAT], int K, int rb, int re, int G, int rc,
-                      const uint8_t* xs, const float2* sb, Sink sink) {
-  constexpr int D = NMAT == 2 ? 3 : 4;  // units in flight per lane
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int sub = 64 / G, g = lane & (G - 1), slot = lane / G;
-  const int U = K >> 5, UPL = U / G, ts = tok_stride(U);
-  const int first = rb + wave * sub, step = kWaves * sub;
-  const int n_rg = first < re ? (re - first + step - 1) / step : 0;
-  const int nflat = n_rg * UPL;
+// Units in flight per lane on the dot-product path: gate and up together
+// hold two units per position.  FEW (the routed FFN, whose blocks are few
+// and short): with one staged row the ring is deeper, so that a block
+// requests most of its weights at once.  Streaming launches (a dense GEMV)
+// keep the shallower ring and their occupancy.
+template <int NMAT, int RC, bool FEW>
+QMOE_HD constexpr int valu_depth() {
+  return NMAT == 2 ? (FEW && RC <= 1 ? 4 : 3) : (FEW && RC <= 1 ? 5 : 4);
+}
 
-  if (nflat == 0) return;  // wave-uniform
-
-  // Every load is unconditional: positions past the wave's last (row group,
-  // unit) re-read the tile's last row, so no load sits behind a branch and
-  // each slot's data is consumed in the registers it was loaded into.
+// The weight stream of one wave over rows [rb, re) of NMAT matrices: lane
+// slot `slot` of each G-lane group takes row first + i * step + slot of row
+// group i and units g, g + G, ... of it.  Positions are flat (row group,
+// unit) pairs in consumption order; every load is unconditional (positions
+// past the wave's last re-read the tile's last row), so no load sits behind
+// a branch and each slot's data is consumed in the registers it was loaded
+// into.
+template <int FMT, int NMAT, int D>
+struct ValuRing {
   Unit<FMT> buf[D][NMAT];
-  int irg = 0, it = 0;  // next (row group, unit) to load
-  auto issue = [&](Unit<FMT> (&w)[NMAT]) {
+  int first, step, re, slot, g, G, UPL, n_rg, nflat;
+  int irg, it;  // next position to load
+
+  // (the wave-uniform fields are moved to scalar registers)
+  QMOE_D ValuRing(int K, int rb, int re_, int G_) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    G = __builtin_amdgcn_readfirstlane(G_);
+    const int sub = 64 / G;
+    g = lane & (G - 1);
+    slot = lane / G;
+    UPL = __builtin_amdgcn_readfirstlane((K >> 5) / G);
+    re = __builtin_amdgcn_readfirstlane(re_);
+    first = __builtin_amdgcn_readfirstlane(rb) + wave * sub;
+    step = kWaves * sub;
+    n_rg = first < re ? (re - first + step - 1) / step : 0;
+    nflat = n_rg * UPL;
+    irg = 0;
+    it = 0;
+  }
+  QMOE_D void issue(const Mat (&mats)[NMAT], int K, int i) {
     const int row = min(first + irg * step + slot, re - 1);
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m) w[m].load(mats[m], row, g + it * G, K);
+    for (int m = 0; m < NMAT; ++m) buf[i][m].load(mats[m], row, g + it * G, K);
     if (++it == UPL) { it = 0; ++irg; }
-  };
+  }
+  // The first D positions, in the order the pass consumes them (the
+  // scheduling barrier keeps the compiler from interleaving them).
+  QMOE_D void prime(const Mat (&mats)[NMAT], int K) {
+    irg = 0;
+    it = 0;
+    if (nflat == 0) return;  // wave-uniform
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      issue(mats, K, i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+};
+
+// Rows [rb, re) of NMAT matrices [*, K] against the rc (<= RC) staged rows,
+// streaming through a primed ring.  sink(row, r, const float* v[NMAT]) is
+// called once per (row, r).  NO_TAIL: the last round issues no loads (a
+// few-row block then ends without loads in flight; elsewhere the second copy
+// of the round costs more instruction cache than the loads cost time).
+template <int FMT, int NMAT, int RC, int D, bool NO_TAIL, class Sink>
+QMOE_D void valu_pass(const Mat (&mats)[NMAT], int K, ValuRing<FMT, NMAT, D>& ring, int rc,
+                      const uint8_t* xs, const float2* sb, Sink sink) {
+  const int G = ring.G, g = ring.g, UPL = ring.UPL;
+  const int U = K >> 5, ts = tok_stride(U);
+  if (ring.nflat == 0) return;  // wave-uniform
+
   auto compute = [&](Unit<FMT> (&w)[NMAT], int u, float (&acc)[NMAT][RC]) {
     // decode every matrix's unit once, then take the staged rows one at a
     // time (one row's activations live in registers at a time)
@@ -359,14 +409,6 @@ QMOE_D void valu_pass(const Mat (&mats)[NMAT], int K, int rb, int re, int G, int
     }
   };
 
-  // The slots are filled in the order the loop consumes them (the barrier
-  // keeps the scheduler from interleaving them), so before each compute the
-  // wait leaves the younger slots' loads in flight.
-#pragma unroll
-  for (int i = 0; i < D; ++i) {
-    issue(buf[i]);
-    __builtin_amdgcn_sched_barrier(0);
-  }
   float acc[NMAT][RC];
 #pragma unroll
   for (int m = 0; m < NMAT; ++m)
@@ -374,19 +416,19 @@ QMOE_D void valu_pass(const Mat (&mats)[NMAT], int K, int rb, int re, int G, int
     for (int r = 0; r < RC; ++r) acc[m][r] = 0.f;
   int crg = 0, ct = 0;  // (row group, unit) being computed
   // nflat rounded up to a multiple of D: the extra positions are computed on
-  // re-read data and never stored (their row group is past the last)
-  for (int f0 = 0; f0 < nflat; f0 += D) {
+  // re-read data and never stored (their row group is past the last).
+  auto round = [&](bool refill) {
 #pragma unroll
     for (int i = 0; i < D; ++i) {
-      compute(buf[i], g + ct * G, acc);
-      issue(buf[i]);
+      compute(ring.buf[i], g + ct * G, acc);
+      if (refill) ring.issue(mats, K, i);
       if (++ct == UPL) {  // wave-uniform
 #pragma unroll
         for (int m = 0; m < NMAT; ++m)
 #pragma unroll
           for (int r = 0; r < RC; ++r) acc[m][r] = group_reduce(acc[m][r], G);
-        const int row = first + crg * step + slot;
-        if (crg < n_rg && row < re && g == G - 1) {
+        const int row = ring.first + crg * ring.step + ring.slot;
+        if (crg < ring.n_rg && row < ring.re && g == G - 1) {
 #pragma unroll
           for (int r = 0; r < RC; ++r) {
             if (r < rc) {
@@ -405,38 +447,74 @@ QMOE_D void valu_pass(const Mat (&mats)[NMAT], int K, int rb, int re, int G, int
         ++crg;
       }
     }
+  };
+  if constexpr (NO_TAIL) {
+    int f0 = 0;
+    for (; f0 + D < ring.nflat; f0 += D) round(true);
+    round(false);
+  } else {
+    for (int f0 = 0; f0 < ring.nflat; f0 += D) round(true);
   }
 }
 
 // Stage up to `chunk` (<= RC) rows at a time and stream the tile against
-// them.
-template <int FMT, int NMAT, int RC, bool COH = false, class SrcOf, class SinkOf>
+// them.  FEW, with at most two rows per chunk and one staged unit per thread:
+// each chunk's first weight units are requested right after its activations,
+// so that both are in flight together (staging four rows needs the registers
+// the ring would hold).
+template <int FMT, int NMAT, int RC, bool COH = false, bool FEW = false, class SrcOf,
+          class SinkOf>
 QMOE_D void valu_rows(const Mat (&mats)[NMAT], int K, int rb, int re, int G, int rows_total,
                       int dtype, uint8_t* lds, SrcOf src_of, SinkOf sink_of, int chunk = RC) {
+  constexpr int D = valu_depth<NMAT, RC, FEW>();
+  constexpr bool kPrimeFirst = FEW && RC <= 2;
   const int U = K >> 5;
   uint8_t* xs = lds;
   float2* sb = (float2*)(lds + (size_t)chunk * tok_stride(U));
   for (int c0 = 0; c0 < rows_total; c0 += chunk) {
     const int rc = min(chunk, rows_total - c0);
-    __syncthreads();
-    stage_rows<FMT, COH>(xs, sb, rc, U, [&](int r) { return src_of(c0 + r); }, dtype);
-    __syncthreads();
     // the register blocking of the pass follows this chunk's row count, so
     // an expert with one row does not pay for the dots of RC rows
     auto sink = [&](int n, int r, const float* a) { sink_of(n, c0 + r, a); };
-    if constexpr (RC >= 4) {
-      if (rc > 2) {
-        valu_pass<FMT, NMAT, 4>(mats, K, rb, re, G, rc, xs, sb, sink);
-        continue;
+    auto pass = [&](ValuRing<FMT, NMAT, D>& ring) {
+      if constexpr (RC >= 4) {
+        if (rc > 2) {
+          valu_pass<FMT, NMAT, 4, D, kPrimeFirst>(mats, K, ring, rc, xs, sb, sink);
+          return;
+        }
       }
-    }
-    if constexpr (RC >= 2) {
-      if (rc == 2) {
-        valu_pass<FMT, NMAT, 2>(mats, K, rb, re, G, rc, xs, sb, sink);
-        continue;
+      if constexpr (RC >= 2) {
+        if (rc == 2) {
+          valu_pass<FMT, NMAT, 2, D, kPrimeFirst>(mats, K, ring, rc, xs, sb, sink);
+          return;
+        }
       }
+      valu_pass<FMT, NMAT, 1, D, kPrimeFirst>(mats, K, ring, rc, xs, sb, sink);
+    };
+    // early (block-uniform): one unit of one row per thread.  Loads complete
+    // in issue order, so the activation loads go first: converting them then
+    // waits only for them, with the weight loads still in flight.  Every
+    // thread loads (the spare ones re-read the last unit) and only the first
+    // rc * U store.
+    const bool early = kPrimeFirst && rc * U <= kBlock;
+    ValuRing<FMT, NMAT, D> ring(K, rb, re, G);
+    const int idx = min((int)threadIdx.x, rc * U - 1);
+    const int r = idx / U, u = idx - r * U;
+    float v[32];
+    if (early) {
+      load32<COH>(src_of(c0 + r), dtype, u, v);
+      __builtin_amdgcn_sched_barrier(0);
+      ring.prime(mats, K);
     }
-    valu_pass<FMT, NMAT, 1>(mats, K, rb, re, G, rc, xs, sb, sink);
+    __syncthreads();  // earlier readers of the LDS are done
+    if (early) {
+      if ((int)threadIdx.x < rc * U) stage_unit<FMT>(xs, sb, r, u, U, v);
+    } else {
+      stage_rows<FMT, COH>(xs, sb, rc, U, [&](int rr) { return src_of(c0 + rr); }, dtype);
+    }
+    __syncthreads();
+    if (!early) ring.prime(mats, K);
+    pass(ring);
   }
 }
 
@@ -726,36 +804,59 @@ QMOE_D float silu_mul(float g, float u) { return g / (1.f + expf(-g)) * u; }
 // Block schedule.  Experts with more than m_max rows ("big") come first with
 // ntiles_big blocks each, then the experts with 1..m_max rows with ntiles
 // blocks each, both groups in id order.  Returns the expert of block b (-1
-// past the end) and sets its tile index and group.  offs (E+1 entries) and
-// red (2 * kWaves + 2 ints) are in LDS.  Block-wide; every thread gets the
-// result.  Experts never routed to have no rows and are never scheduled, nor
-// are ids outside [0, E) ([P2] bug items 1 and 3).
-QMOE_D int scheduled_expert(const int* offs, int E, int m_max, int b, int ntiles,
-                            int ntiles_big, int* red, int& tile, bool& big) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// past the end) and sets its tile index, group, first position pos0 and row
+// count m.  Thread t reads the row counts of experts [t per, (t + 1) per)
+// from the offsets (E + 1 entries, global memory); the counts' prefix over
+// the wave comes from ballots (one per bit of a thread's count), over the
+// waves from red (2 * kWaves + 3 ints of LDS).  Block-wide; every thread gets
+// the result.  Experts never routed to have no rows and are never scheduled,
+// nor are ids outside [0, E) ([P2] bug items 1 and 3).
+constexpr int kSchedRedInts = 2 * kWaves + 3;
+
+QMOE_D int scheduled_expert(const int32_t* offsets, int E, int m_max, int b, int ntiles,
+                            int ntiles_big, int* red, int& tile, bool& big, int& pos0,
+                            int& m_out) {
+  const int tid = threadIdx.x, wave = tid >> 6;
   const int per = (E + kBlock - 1) / kBlock;
   const int lo = min(E, tid * per), hi = min(E, lo + per);
   int nb = 0, ns = 0;
-  for (int e = lo; e < hi; ++e) {
-    const int m = offs[e + 1] - offs[e];
-    nb += m > m_max;
-    ns += m > 0 && m <= m_max;
+  {
+    int prev = lo < hi ? offsets[lo] : 0;
+    for (int e0 = lo; e0 < hi; e0 += 4) {
+      int nx[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) nx[j] = e0 + j < hi ? offsets[e0 + j + 1] : 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (e0 + j < hi) {
+          const int m = nx[j] - prev;
+          nb += m > m_max;
+          ns += m > 0 && m <= m_max;
+          prev = nx[j];
+        }
+      }
+    }
   }
-  int sb = nb, ss = ns;  // inclusive scans within the wave
-  for (int off = 1; off < 64; off <<= 1) {
-    const int ob = __shfl_up(sb, off, 64), os = __shfl_up(ss, off, 64);
-    if (lane >= off) { sb += ob; ss += os; }
+  // exclusive prefixes within the wave and wave totals, bit by bit
+  int xb = 0, xs = 0, wb = 0, ws = 0;
+  for (int bit = 0; (1 << bit) <= per; ++bit) {
+    const uint64_t bb = __ballot((nb >> bit) & 1), bs = __ballot((ns >> bit) & 1);
+    xb += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bb >> 32),
+                                         __builtin_amdgcn_mbcnt_lo((uint32_t)bb, 0u)) << bit;
+    xs += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bs >> 32),
+                                         __builtin_amdgcn_mbcnt_lo((uint32_t)bs, 0u)) << bit;
+    wb += __popcll(bb) << bit;
+    ws += __popcll(bs) << bit;
   }
-  if (lane == 63) { red[wave] = sb; red[kWaves + wave] = ss; }
+  if ((tid & 63) == 0) { red[wave] = wb; red[kWaves + wave] = ws; }
   if (tid == 0) red[2 * kWaves] = -1;
   __syncthreads();
-  int bb = 0, bs = 0, tb = 0, ts = 0;
+  int tb = 0, ts = 0;
   for (int w = 0; w < kWaves; ++w) {
-    if (w < wave) { bb += red[w]; bs += red[kWaves + w]; }
+    if (w < wave) { xb += red[w]; xs += red[kWaves + w]; }
     tb += red[w];
     ts += red[kWaves + w];
   }
-  const int xb = bb + sb - nb, xs = bs + ss - ns;  // exclusive prefixes of this slice
   const long long big_blocks = (long long)tb * ntiles_big;
   big = b < big_blocks;
   const int rel = big ? b : (int)(b - big_blocks);
@@ -766,14 +867,21 @@ QMOE_D int scheduled_expert(const int* offs, int E, int m_max, int b, int ntiles
   if ((big || want < ts) && want >= first && want < first + count) {
     int c = first;
     for (int e = lo; e < hi; ++e) {
-      const int m = offs[e + 1] - offs[e];
+      const int p0 = offsets[e], m = offsets[e + 1] - p0;
       if (big ? m > m_max : (m > 0 && m <= m_max)) {
-        if (c == want) { red[2 * kWaves] = e; break; }
+        if (c == want) {
+          red[2 * kWaves] = e;
+          red[2 * kWaves + 1] = p0;
+          red[2 * kWaves + 2] = m;
+          break;
+        }
         ++c;
       }
     }
   }
   __syncthreads();
+  pos0 = red[2 * kWaves + 1];
+  m_out = red[2 * kWaves + 2];
   return red[2 * kWaves];
 }
 
@@ -836,14 +944,15 @@ QMOE_D void ffn_item(const FfnParams& P, int e, int tile, bool big, int pos0, in
         mfma_cols<FM, 2, QMOE_F32>(mats, K, rb, re, m, smem, x_row, h_out);                \
       else if (MFMA && big)                                                                \
         mfma_cols<FM, 2, QMOE_BF16>(mats, K, rb, re, m, smem, x_row, h_out);               \
-      else valu_rows<FM, 2, RC>(mats, K, rb, re, G, m, dtype, smem, x_row, h_out, chunk);  \
+      else valu_rows<FM, 2, RC, false, true>(mats, K, rb, re, G, m, dtype, smem, x_row,     \
+                                             h_out, chunk);                                \
     } else {                                                                               \
       const Mat mats[1] = {mat_of((const uint8_t*)t.down + eo, FM, N, K)};                 \
       if (MFMA && big)                                                                     \
         mfma_cols<FM, 1, COH ? kF32Coherent : QMOE_F32>(mats, K, rb, re, m, smem, h_row,   \
                                                         o_out);                            \
-      else valu_rows<FM, 1, RC, COH>(mats, K, rb, re, G, m, QMOE_F32, smem, h_row, o_out,  \
-                                     chunk);                                               \
+      else valu_rows<FM, 1, RC, COH, true>(mats, K, rb, re, G, m, QMOE_F32, smem, h_row,   \
+                                           o_out, chunk);                                  \
     }                                                                                      \
   } break;
   switch (fmt) {

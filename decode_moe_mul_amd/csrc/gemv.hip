@@ -126,28 +126,26 @@ __global__ __launch_bounds__(kBlock) void qgemv_batch_kernel(GemvBatchParams P) 
 
 // PHASE 0: gate/up + SwiGLU -> h;  PHASE 1: down -> o.  MFMA: whether
 // experts with more than m_max rows can occur (the matrix-core branch costs
-// registers, so launches that cannot use it leave it out).
+// registers, so launches that cannot use it leave it out).  Gate/up blocks
+// take the registers of two blocks per compute unit (gate and up tiles at
+// once, or a deep ring of weight loads for one row), down blocks of three.
 template <int PHASE, int RC, bool MFMA>
-__global__ __launch_bounds__(kBlock, (PHASE == 1 || RC <= 2) ? 3 : 2) void ffn_decode_kernel(FfnParams P) {
+__global__ __launch_bounds__(kBlock, PHASE == 1 ? 3 : 2) void ffn_decode_kernel(FfnParams P) {
   extern __shared__ __align__(16) uint8_t smem[];
-  const int E = P.E;
   const int32_t* perm = P.perm;
-  int* offs = (int*)smem;
-  int* red = offs + E + 1;
-  for (int i = threadIdx.x; i <= E; i += kBlock) offs[i] = P.offsets[i];
-  __syncthreads();
-  int tile = 0;
+  int* red = (int*)smem;
+  int tile = 0, pos0 = 0, m = 0;
   bool big = false;
   // block-uniform values read from LDS, moved to scalar registers so that
   // the weight bases derived from them stay scalar (loads then take a
   // scalar base and a 32-bit vector offset)
-  const int e = __builtin_amdgcn_readfirstlane(
-      scheduled_expert(offs, E, P.m_max, blockIdx.x, P.ntiles, P.ntiles_big, red, tile, big));
+  const int e = __builtin_amdgcn_readfirstlane(scheduled_expert(
+      P.offsets, P.E, P.m_max, blockIdx.x, P.ntiles, P.ntiles_big, red, tile, big, pos0, m));
   if (e < 0) return;
   tile = __builtin_amdgcn_readfirstlane(tile);
   big = __builtin_amdgcn_readfirstlane((int)big) != 0;
-  const int pos0 = __builtin_amdgcn_readfirstlane(offs[e]);
-  const int m = __builtin_amdgcn_readfirstlane(offs[e + 1]) - pos0;
+  pos0 = __builtin_amdgcn_readfirstlane(pos0);
+  m = __builtin_amdgcn_readfirstlane(m);
   ffn_item<PHASE, RC, MFMA, false, false>(P, e, tile, big, pos0, m, smem,
                                           [=](int i) { return perm[i]; });
 }
@@ -414,7 +412,7 @@ int moe_ffn_tiered(const qmoe_tier* tiers, int n_tiers, int E, int H, int F, con
   P.x = x; P.x_dtype = x_dtype; P.offsets = offsets; P.perm = perm;
   P.h = (float*)ws; P.o = o;
   const int ranks = (int)(A < E ? A : E);  // experts that can receive rows
-  const size_t sched_bytes = (size_t)(E + 1 + 2 * kWaves + 2) * 4;
+  const size_t sched_bytes = (size_t)kSchedRedInts * 4;
   // Experts with more rows than the dot-product path blocks in registers
   // use the matrix cores, when the row count allows that to happen (with
   // duplicate ids the dot-product path loops over row chunks instead).

@@ -37,17 +37,35 @@ QMOE_D void permute_block(const int32_t* ids, int A, int E, int W, int nbits, in
   for (int i = threadIdx.x; i < W * E; i += NT) hist[i] = 0;
   __syncthreads();
   const long long a_begin = (long long)wave * A / W, a_end = (long long)(wave + 1) * A / W;
+  // The ids of kIdBatch 64-chunks are loaded together (every lane loads; past
+  // the range it re-reads the range's last id), so a pass waits for memory
+  // once per batch rather than once per chunk.
+  constexpr int kIdBatch = 8;
+  auto load_batch = [&](long long c0, int (&idb)[kIdBatch]) {
+#pragma unroll
+    for (int j = 0; j < kIdBatch; ++j) {
+      const long long a = c0 + 64 * j + lane;
+      idb[j] = ids[a < a_end ? a : a_end - 1];
+    }
+  };
   // pass 1: per-wave histogram
-  if (wave < W) {
-    for (long long c = a_begin; c < a_end; c += 64) {
-      const long long a = c + lane;
-      const bool in = a < a_end;
-      const int id = in ? ids[a] : -1;
-      const bool valid = in && id >= 0 && id < E;
-      const uint64_t active = __ballot(valid);
-      const uint64_t peers = peers_of(valid ? id : 0, nbits, active);
-      if (valid && (peers & lanes_below(lane)) == 0)
-        hist[wave * E + id] += __popcll(peers);
+  if (wave < W && a_begin < a_end) {
+    for (long long c0 = a_begin; c0 < a_end; c0 += 64 * kIdBatch) {
+      int idb[kIdBatch];
+      load_batch(c0, idb);
+#pragma unroll
+      for (int j = 0; j < kIdBatch; ++j) {
+        const long long c = c0 + 64 * j;
+        if (c >= a_end) break;  // wave-uniform
+        const long long a = c + lane;
+        const bool in = a < a_end;
+        const int id = idb[j];
+        const bool valid = in && id >= 0 && id < E;
+        const uint64_t active = __ballot(valid);
+        const uint64_t peers = peers_of(valid ? id : 0, nbits, active);
+        if (valid && (peers & lanes_below(lane)) == 0)
+          hist[wave * E + id] += __popcll(peers);
+      }
     }
   }
   __syncthreads();
@@ -81,25 +99,32 @@ QMOE_D void permute_block(const int32_t* ids, int A, int E, int W, int nbits, in
   if (threadIdx.x == 0) offsets[E] = total;
   __syncthreads();
   // pass 2: stable scatter within each wave's range
-  if (wave < W) {
-    for (long long c = a_begin; c < a_end; c += 64) {
-      const long long a = c + lane;
-      const bool in = a < a_end;
-      const int id = in ? ids[a] : -1;
-      const bool valid = in && id >= 0 && id < E;
-      const uint64_t active = __ballot(valid);
-      const uint64_t peers = peers_of(valid ? id : 0, nbits, active);
-      if (valid) {
-        const int pos = hist[wave * E + id] + __popcll(peers & lanes_below(lane));
-        perm[pos] = (int32_t)a;
-        inv[a] = pos;
-      } else if (in) {
-        inv[a] = -1;
+  if (wave < W && a_begin < a_end) {
+    for (long long c0 = a_begin; c0 < a_end; c0 += 64 * kIdBatch) {
+      int idb[kIdBatch];
+      load_batch(c0, idb);
+#pragma unroll
+      for (int j = 0; j < kIdBatch; ++j) {
+        const long long c = c0 + 64 * j;
+        if (c >= a_end) break;  // wave-uniform
+        const long long a = c + lane;
+        const bool in = a < a_end;
+        const int id = idb[j];
+        const bool valid = in && id >= 0 && id < E;
+        const uint64_t active = __ballot(valid);
+        const uint64_t peers = peers_of(valid ? id : 0, nbits, active);
+        if (valid) {
+          const int pos = hist[wave * E + id] + __popcll(peers & lanes_below(lane));
+          perm[pos] = (int32_t)a;
+          inv[a] = pos;
+        } else if (in) {
+          inv[a] = -1;
+        }
+        // all lanes have read their cursor; now the leaders advance it
+        __builtin_amdgcn_wave_barrier();
+        if (valid && (peers & lanes_below(lane)) == 0) hist[wave * E + id] += __popcll(peers);
+        __builtin_amdgcn_wave_barrier();
       }
-      // all lanes have read their cursor; now the leaders advance it
-      __builtin_amdgcn_wave_barrier();
-      if (valid && (peers & lanes_below(lane)) == 0) hist[wave * E + id] += __popcll(peers);
-      __builtin_amdgcn_wave_barrier();
     }
   }
   // positions past the valid ones hold -1

@@ -507,10 +507,9 @@ QMOE_D void tile_mx(const PrefillParams& P, const void* W0, const void* W1, int 
   }
 }
 
-// Tiles of more than kSmall rows (up to kBM) and tiles of at most kSmall
-// rows run in separate launches: each kernel's registers and LDS are sized
-// for its own tile height, so the short tiles (experts with a few rows,
-// whose time is the weight stream) run at a higher occupancy.
+// Tiles of more than kSmall rows (up to kBM) take 16 kMI-row register
+// blocks; tiles of at most kSmall rows (experts with a few rows, whose time is
+// the weight stream) take kMIsmall-row blocks.
 constexpr int kSmall = 32;
 constexpr int kMIsmall = kSmall / 16;
 
@@ -523,50 +522,62 @@ QMOE_D void tile_dispatch_full(const PrefillParams& P, const void* W0, const voi
     tile_gemm<FMT, PASS, NB, MI, false>(P, W0, W1, pos0, cnt, nt, As);
 }
 
-// Persistent: block b takes work items b, b + gridDim.x, ... of the list's
-// (tile, column tile) items.  Item w runs on XCD w & 7 (the grid is a multiple
+// Work item (tile of list `list`, column tile nt) with MI-row register blocks.
+template <int PASS, int NB, int MI, bool MXP>
+QMOE_D void prefill_item(const PrefillParams& P, int list, int tile, int nt, uint16_t* As) {
+  const int2 te = P.tiles[(list ? P.tiles_cap_big : 0) + tile];
+  const int e = te.x;
+  qmoe_tier t;
+  if (!prefill_tier(P, e, t)) return;
+  const int pos0 = P.offsets[e] + te.y * kBM;
+  const int cnt = min(kBM, P.offsets[e + 1] - pos0);
+  const int fmt = PASS == 1 ? t.fmt_gate_up : t.fmt_down;
+  const int N = PASS == 1 ? P.F : P.H, K = PASS == 1 ? P.H : P.F;
+  const size_t eo = (size_t)(e - t.e_begin) * layout_of(fmt, N, K).total;
+  const uint8_t* W0 = (const uint8_t*)(PASS == 1 ? t.gate : t.down) + eo;
+  const uint8_t* W1 = (const uint8_t*)t.up + eo;
+  switch (fmt) {
+    case QMOE_Q8_0: tile_dispatch_full<QMOE_Q8_0, PASS, NB, MI>(P, W0, W1, pos0, cnt, nt, As); break;
+    case QMOE_Q4_0: tile_dispatch_full<QMOE_Q4_0, PASS, NB, MI>(P, W0, W1, pos0, cnt, nt, As); break;
+    case QMOE_MXFP4:
+      if constexpr (MXP) {
+        if (t.fmt_gate_up == QMOE_MXFP4 && t.fmt_down == QMOE_MXFP4) {
+          tile_mx<PASS, NB, MI>(P, W0, W1, pos0, cnt, nt, (float*)As);
+          break;
+        }
+      }
+      tile_dispatch_full<QMOE_MXFP4, PASS, NB, MI>(P, W0, W1, pos0, cnt, nt, As);
+      break;
+    case QMOE_Q4_K: tile_dispatch_full<QMOE_Q4_K, PASS, NB, MI>(P, W0, W1, pos0, cnt, nt, As); break;
+    case QMOE_Q6_K: tile_dispatch_full<QMOE_Q6_K, PASS, NB, MI>(P, W0, W1, pos0, cnt, nt, As); break;
+    default: break;
+  }
+}
+
+// Persistent, one launch per pass: block b takes work items b, b + gridDim.x,
+// ... of the (tile, column tile) items of the big-tile list, then of the
+// small-tile list, so that the many-row tiles (bound by the matrix cores) and
+// the few-row tiles (bound by the weight stream) run side by side.  Item w of
+// a list runs on XCD w & 7 (the grid and each list's item count are multiples
 // of 8); the column tiles of one row tile share an XCD and follow each other
 // there, so its staged activation rows are read from that XCD's L2.
 // MXP: MXFP4/MXFP4 tiers take the block-scaled path (instantiated apart, so
 // the plain kernels keep their registers).
-template <int PASS, int NB, int MI, bool MXP>
-__global__ __launch_bounds__(kPB, MI == kMIsmall ? 3 : 2) void prefill_kernel(PrefillParams P, int list) {
-  __shared__ __align__(16) uint16_t As[2 * 16 * MI * kAS];
-  const int2* tiles = P.tiles + (list ? P.tiles_cap_big : 0);
-  const int count = P.counts[list];
+template <int PASS, int NB, bool MXP>
+__global__ __launch_bounds__(kPB, 2) void prefill_kernel(PrefillParams P) {
+  __shared__ __align__(16) uint16_t As[2 * 16 * kMI * kAS];
   const int ntl = P.ntiles;
-  const int items = (count + 7) / 8 * 8 * ntl;
-  for (int w = blockIdx.x; w < items; w += gridDim.x) {
+  const int count_big = P.counts[0], count_small = P.counts[1];
+  const int items_big = (count_big + 7) / 8 * 8 * ntl;
+  const int items = items_big + (count_small + 7) / 8 * 8 * ntl;
+  for (int w0 = blockIdx.x; w0 < items; w0 += gridDim.x) {
+    const bool big = w0 < items_big;  // block-uniform
+    const int w = big ? w0 : w0 - items_big;
     const int slot = w >> 3;
     const int tile = (slot / ntl) * 8 + (w & 7), nt = slot - (slot / ntl) * ntl;
-    if (tile >= count) continue;  // block-uniform
-    const int2 te = tiles[tile];
-    const int e = te.x;
-    qmoe_tier t;
-    if (!prefill_tier(P, e, t)) continue;
-    const int pos0 = P.offsets[e] + te.y * kBM;
-    const int cnt = min(kBM, P.offsets[e + 1] - pos0);
-    const int fmt = PASS == 1 ? t.fmt_gate_up : t.fmt_down;
-    const int N = PASS == 1 ? P.F : P.H, K = PASS == 1 ? P.H : P.F;
-    const size_t eo = (size_t)(e - t.e_begin) * layout_of(fmt, N, K).total;
-    const uint8_t* W0 = (const uint8_t*)(PASS == 1 ? t.gate : t.down) + eo;
-    const uint8_t* W1 = (const uint8_t*)t.up + eo;
-    switch (fmt) {
-      case QMOE_Q8_0: tile_dispatch_full<QMOE_Q8_0, PASS, NB, MI>(P, W0, W1, pos0, cnt, nt, As); break;
-      case QMOE_Q4_0: tile_dispatch_full<QMOE_Q4_0, PASS, NB, MI>(P, W0, W1, pos0, cnt, nt, As); break;
-      case QMOE_MXFP4:
-        if constexpr (MXP) {
-          if (t.fmt_gate_up == QMOE_MXFP4 && t.fmt_down == QMOE_MXFP4) {
-            tile_mx<PASS, NB, MI>(P, W0, W1, pos0, cnt, nt, (float*)As);
-            break;
-          }
-        }
-        tile_dispatch_full<QMOE_MXFP4, PASS, NB, MI>(P, W0, W1, pos0, cnt, nt, As);
-        break;
-      case QMOE_Q4_K: tile_dispatch_full<QMOE_Q4_K, PASS, NB, MI>(P, W0, W1, pos0, cnt, nt, As); break;
-      case QMOE_Q6_K: tile_dispatch_full<QMOE_Q6_K, PASS, NB, MI>(P, W0, W1, pos0, cnt, nt, As); break;
-      default: break;
-    }
+    if (tile >= (big ? count_big : count_small)) continue;  // block-uniform
+    if (big) prefill_item<PASS, NB, kMI, MXP>(P, 0, tile, nt, As);
+    else prefill_item<PASS, NB, kMIsmall, MXP>(P, 1, tile, nt, As);
   }
 }
 
@@ -743,29 +754,20 @@ static size_t prefill_workspace_bytes(int T, int k, int E, int H, int F) {
          256 + 256 + mx_bytes(T + 1, step_round(H)) + mx_bytes(A + 1, step_round(F));
 }
 
-// per pass: the big-tile list, then the small-tile list
+// one launch per pass (both tile lists)
 template <bool MXP>
 static int prefill_launch(PrefillParams P, hipStream_t s) {
-  static int grid[2][2] = {{0, 0}, {0, 0}};
-  if (!grid[0][0]) {
-    grid[0][0] = persistent_grid(prefill_kernel<1, kNB1, kMI, MXP>);
-    grid[0][1] = persistent_grid(prefill_kernel<1, kNB1, kMIsmall, MXP>);
-    grid[1][0] = persistent_grid(prefill_kernel<2, kNB2, kMI, MXP>);
-    grid[1][1] = persistent_grid(prefill_kernel<2, kNB2, kMIsmall, MXP>);
+  static int grid[2] = {0, 0};
+  if (!grid[0]) {
+    grid[0] = persistent_grid(prefill_kernel<1, kNB1, MXP>);
+    grid[1] = persistent_grid(prefill_kernel<2, kNB2, MXP>);
   }
   P.ntiles = (P.F + kPW * kNB1 * 16 - 1) / (kPW * kNB1 * 16);
-  int st = QMOE_LAUNCH("prefill_gate_up", (prefill_kernel<1, kNB1, kMI, MXP>), dim3(grid[0][0]),
-                       kPB, 0, s, P, 0);
-  if (st) return st;
-  st = QMOE_LAUNCH("prefill_gate_up", (prefill_kernel<1, kNB1, kMIsmall, MXP>),
-                   dim3(grid[0][1]), kPB, 0, s, P, 1);
+  int st = QMOE_LAUNCH("prefill_gate_up", (prefill_kernel<1, kNB1, MXP>), dim3(grid[0]), kPB, 0,
+                       s, P);
   if (st) return st;
   P.ntiles = (P.H + kPW * kNB2 * 16 - 1) / (kPW * kNB2 * 16);
-  st = QMOE_LAUNCH("prefill_down", (prefill_kernel<2, kNB2, kMI, MXP>), dim3(grid[1][0]), kPB, 0,
-                   s, P, 0);
-  if (st) return st;
-  return QMOE_LAUNCH("prefill_down", (prefill_kernel<2, kNB2, kMIsmall, MXP>), dim3(grid[1][1]),
-                     kPB, 0, s, P, 1);
+  return QMOE_LAUNCH("prefill_down", (prefill_kernel<2, kNB2, MXP>), dim3(grid[1]), kPB, 0, s, P);
 }
 
 static int prefill_run(const char* who, bool mx, const qmoe_tier* tiers, int n_tiers, int E,
