@@ -716,6 +716,24 @@ def stream_ceiling(torch, reps=20):
     del buf
     torch.cuda.empty_cache()
     log(f"streaming-read ceiling: {best} GB/s")
+    # the floor of a chain of dependent launches: reads of 4 KiB (one block
+    # per CU) back to back on one stream, each waiting for the last; captured
+    # as one graph of 200 launches so that the host's enqueue rate is out of
+    # the measurement (eager: the host's rate bounds it)
+    tiny = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    n = 200
+    qmoe.stream_read(tiny, 1, sink)
+    out["launch_chain_eager_us"] = round(
+        _events_ms(torch, lambda i: qmoe.stream_read(tiny, 1, sink), n) * 1e3, 2)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(n):
+            qmoe.stream_read(tiny, 1, sink)
+    g.replay()
+    out["launch_chain_graph_us"] = round(_events_ms(torch, lambda i: g.replay(), 10) * 1e3 / n, 2)
+    del g
+    log(f"dependent launches: {out['launch_chain_graph_us']} us each in a graph, "
+        f"{out['launch_chain_eager_us']} us eager")
     return out
 
 
@@ -761,7 +779,7 @@ def main():
     ap.add_argument("--prefill-only", action="store_true",
                     help="run only the 2048-row prefill section (prefill counter runs)")
     ap.add_argument("--one-launch", action="store_true",
-                    help="also time the retired one-launch layer (a cooperative launch)")
+                    help="also time the one-launch layer (moe_layer_decode) at 1 and 6 rows")
     ap.add_argument("--graph-iters", type=int, default=500)
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
                     help="print the per-kernel table of a rocprofv3 --kernel-trace run and exit")

@@ -282,7 +282,7 @@ typedef struct qmoe_tier {
  * not written.  offsets/perm are moe_permute's.  x as in moe_route; |x| and
  * |h| must stay below 65504 (fp16 inside the dot products).  An expert with
  * more rows than the dot-product blocking (1, 2 or 4 rows, set by T and by
- * how many staged rows of length H or F fit in 64 KB of LDS) runs on the
+ * how many staged rows of length H or F fit in 96 KB of LDS) runs on the
  * matrix cores against the exact weight codes (the unit scale multiplies
  * the fp32 result), so only the activations are rounded, as in qgemv.
  * Limits: n_tiers <= QMOE_MAX_TIERS; H, F <= 65536.
