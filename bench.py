@@ -713,6 +713,25 @@ def stream_ceiling(torch, reps=20):
     best = max(out["per_blocks_per_cu"].values())
     out["gbs"] = best
     out["frac_of_peak"] = round(best / HBM_PEAK_GBS, 4)
+    # the same read at the sizes of the decode workloads (one launch per
+    # read, rotating over 8 disjoint slices so that the last-level cache does
+    # not serve them): what a single weight stream of that size can reach
+    out["at_size"] = {}
+    for name, nb in (("tiered_1row", 37564108), ("tiered_6rows", 143694950),
+                     ("dense_layer", 137822208)):
+        n16 = nb // 16 * 16
+        slices = [buf.view(torch.uint8)[i * (nbytes // 8):i * (nbytes // 8) + n16].view(torch.int32)
+                  for i in range(8)]
+        for sl in slices:
+            qmoe.stream_read(sl, 8, sink)
+        best_us = None
+        for bpc in (4, 8, 16):
+            ms = _events_ms(torch, lambda i: qmoe.stream_read(slices[i % 8], bpc, sink), 40)
+            best_us = ms * 1e3 if best_us is None else min(best_us, ms * 1e3)
+        out["at_size"][name] = {"bytes": n16, "us": round(best_us, 2),
+                                "gbs": round(n16 / (best_us * 1e-6) / 1e9, 1),
+                                "frac_of_peak": round(n16 / (best_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    log(f"streaming read at workload sizes: {out['at_size']}")
     del buf
     torch.cuda.empty_cache()
     log(f"streaming-read ceiling: {best} GB/s")
