@@ -23,15 +23,22 @@ Timed passes (each over the same steps, inputs and weight rotation):
   2. each row count alone: tokens_per_s, ms_per_call;
   3. the library's HIP events around every gate/up launch only: the
      roofline of the dominant kernel (ffn_gate_up);
-  4. events around every launch: kernel_ms_per_step (context only);
-  5. the 1- and 6-row calls as one cooperative launch each
-     (moe_layer_decode): one_launch_layer (context only).
-Also reported: the fraction of the 8 TB/s HBM peak, the gate/up HBM traffic
-from stored counter runs, and the CPU oracle timed on a bounded sample; and,
-outside the step, the dense layer GEMV (Llama-3-8B shapes, Q4_K/Q6_K and the
-ternary T5 format) and the 2048-row prefill chunk.
+  4. events around every launch: kernel_ms_per_step and, per row count, the
+     summed kernel time of a call (per_config);
+  5. each call captured as a HIP graph and replayed (>= 500 replays,
+     median / p10 / p90);
+  6. with --one-launch, the 1- and 6-row calls as one moe_layer_decode
+     launch each: one_launch_layer (context only).
+Also reported: per row count the weight bytes, GB/s and fraction of the 8 TB/s
+HBM peak; the gate/up HBM traffic from stored counter runs; a plain streaming
+read (the part's ceiling, and its rate at the workloads' sizes) and the floor
+of a dependent launch; the CPU oracle timed on a bounded sample of every
+workload; and, outside the step, the dense layer GEMV (Llama-3-8B shapes,
+Q4_K/Q6_K and the ternary T5 format), the 2048-row prefill chunk, the
+block-scaled MX GEMM and the int8 GEMV and GEMM.
 
-    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--no-cpu-baseline] [--decode-only]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu-baseline]
+                    [--decode-only | --prefill-only] [--one-launch]
 """
 import argparse
 import json
