@@ -37,7 +37,7 @@ workload; and, outside the step, the dense layer GEMV (Llama-3-8B shapes,
 Q4_K/Q6_K and the ternary T5 format), the 2048-row prefill chunk, the
 block-scaled MX GEMM and the int8 GEMV and GEMM.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--no-cpu-baseline]
                     [--decode-only | --prefill-only] [--one-launch]
 """
 import argparse
