@@ -289,13 +289,10 @@ __global__ void zero_words_kernel(unsigned* w, int n) {
   for (int i = threadIdx.x; i < n; i += blockDim.x) w[i] = 0u;
 }
 
-// moe_route_decode on the workspace ws; `who` names the entry point in error
-// texts; clear_ctr: zero the block counter first (one small kernel).
-static int route_decode_impl(const char* who, const void* x, int x_dtype, int T, int H,
-                             const float* Wr, const float* bias, int E, int k, int n_shared,
-                             int32_t* ids, float* p, float* logits, int32_t* offsets,
-                             int32_t* perm, int32_t* inv_perm, void* ws, size_t ws_bytes,
-                             bool clear_ctr, void* stream) {
+// The size checks of the fused decode routing (host only, before any device
+// call).
+static int route_decode_sizes(const char* who, int x_dtype, int T, int H, int E, int k,
+                              int n_shared) {
   if (T < 0 || H <= 0 || E <= 0 || k < 1 || k > E || k > 64 || n_shared < 0)
     return fail(QMOE_ERR_INVALID_ARG, "%s: bad sizes T=%d H=%d E=%d k=%d n_shared=%d", who, T,
                 H, E, k, n_shared);
@@ -305,6 +302,18 @@ static int route_decode_impl(const char* who, const void* x, int x_dtype, int T,
   if (H % 4) return fail(QMOE_ERR_INVALID_ARG, "%s: H %% 4 != 0", who);
   if (x_dtype != QMOE_F32 && x_dtype != QMOE_BF16)
     return fail(QMOE_ERR_UNSUPPORTED, "%s: unknown x_dtype %d", who, x_dtype);
+  return QMOE_OK;
+}
+
+// moe_route_decode on the workspace ws; `who` names the entry point in error
+// texts; clear_ctr: zero the block counter first (one small kernel).
+static int route_decode_impl(const char* who, const void* x, int x_dtype, int T, int H,
+                             const float* Wr, const float* bias, int E, int k, int n_shared,
+                             int32_t* ids, float* p, float* logits, int32_t* offsets,
+                             int32_t* perm, int32_t* inv_perm, void* ws, size_t ws_bytes,
+                             bool clear_ctr, void* stream) {
+  const int sz = route_decode_sizes(who, x_dtype, T, H, E, k, n_shared);
+  if (sz) return sz;
   const int kt = k + n_shared, E_total = E + n_shared, A = T * kt;
   const int hist_ints = kDecodeLdsInts - ((A + 63) & ~63) - kGemvBlock / 64;
   if (hist_ints < E_total)
@@ -409,6 +418,8 @@ int moe_route_decode_noalloc(const void* x, int x_dtype, int T, int H, const flo
                              const float* bias, int E, int k, int n_shared, int32_t* ids,
                              float* p, float* logits, int32_t* offsets, int32_t* perm,
                              int32_t* inv_perm, void* stream) {
+  const int sz = route_decode_sizes("moe_route_decode_noalloc", x_dtype, T, H, E, k, n_shared);
+  if (sz) return sz;
   const size_t need = moe_route_decode_workspace_size(T, H, E);
   if (need > kRouteScratchBytes)
     return fail(QMOE_ERR_UNSUPPORTED,

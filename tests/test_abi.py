@@ -214,3 +214,32 @@ def test_int8_gemv_validation(L):
     assert L.qgemv_q8_0_i8(fake, 16, 64, fake, fake, 17, fake, None) == -1  # R > 16
     assert L.qgemv_q8_0_i8(fake, 16, 48, fake, fake, 2, fake, None) == -1   # K % 32
     assert L.qgemv_q8_0_i8(fake, 0, 64, fake, fake, 2, fake, None) == 0
+
+
+def test_newer_entry_points_validate_on_the_host(L):
+    """Argument errors of the int8 GEMM, the streaming read, the one-launch
+    layer and the allocation-free routing are caught before any launch."""
+    from decode_moe_mul_amd import qmoe
+    fake = ctypes.c_void_p(256 * 1000)
+    # qgemm_q8_0_i8: K not a multiple of 32, negative sizes, null pointers
+    assert L.qgemm_q8_0_i8(fake, 64, 48, fake, fake, 16, fake, None) == -1
+    assert L.qgemm_q8_0_i8(fake, -1, 64, fake, fake, 16, fake, None) == -1
+    assert L.qgemm_q8_0_i8(fake, 0, 64, fake, fake, 16, fake, None) == 0      # no rows: no-op
+    assert L.qgemm_q8_0_i8(None, 64, 64, fake, fake, 16, fake, None) == -1
+    assert L.qgemm_q8_0_i8(ctypes.c_void_p(256 * 1000 + 16), 64, 64, fake, fake, 16, fake,
+                           None) == -1                                          # W misaligned
+    # qmoe_stream_read: sizes, alignment, blocks per CU
+    assert L.qmoe_stream_read(fake, 0, 8, fake, None) == 0
+    assert L.qmoe_stream_read(fake, 24, 8, fake, None) == -1
+    assert L.qmoe_stream_read(ctypes.c_void_p(256 * 1000 + 4), 64, 8, fake, None) == -1
+    assert L.qmoe_stream_read(fake, 64, 0, fake, None) == -1
+    assert L.qmoe_stream_read(fake, 64, 65, fake, None) == -1
+    assert L.qmoe_stream_read(fake, 64, 8, None, None) == -1
+    # moe_layer_decode: more than 16 rows, more than 512 experts
+    t = (qmoe.Tier * 1)(qmoe.Tier(0, 8, 0, 0, 256000, 256000, 256000))
+    args = (fake, fake, fake, fake, fake, fake, fake, 1 << 20, None)
+    assert L.moe_layer_decode(t, 1, 8, 64, 64, fake, 0, 17, fake, None, 2, 0, *args) == -2
+    assert L.moe_layer_decode(t, 1, 600, 64, 64, fake, 0, 4, fake, None, 2, 0, *args) == -2
+    # moe_route_decode_noalloc: more rows than the fused routing takes
+    assert L.moe_route_decode_noalloc(fake, 0, 17, 64, fake, None, 16, 2, 0, fake, fake, None,
+                                      fake, fake, fake, None) == -2
