@@ -166,6 +166,73 @@ QMOE_D void permute_small(const int32_t* ids, int A, int E, int32_t* offsets, in
   for (int i = total + threadIdx.x; i < A; i += NT) perm[i] = -1;
 }
 
+// Inclusive prefix sum over the wave (DPP row shifts, then row broadcasts;
+// lanes whose source is out of range add 0).
+QMOE_D int wave_prefix_sum(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return v;
+}
+
+// The same stable order for decode routing output: assignment a = t * kt + j
+// of row t < T <= 32, where a row never names an expert twice (a top-k
+// followed by distinct shared experts).  Each expert records the set of rows
+// that chose it as a bit mask (LDS atomic or); offsets are the block's prefix
+// sum of the masks' popcounts, and a row's rank within its expert is the
+// number of earlier rows in the mask, which is the number of earlier equal
+// ids.  lds holds 2 E + 1 + NT/64 ints.  Called by every thread of the block.
+template <int NT>
+QMOE_D void permute_rows(const int32_t* ids, int T, int kt, int E, int32_t* offsets,
+                         int32_t* perm, int32_t* inv, int* lds) {
+  uint32_t* rows = (uint32_t*)lds;  // [E]
+  int* offs = lds + E;              // [E + 1]
+  int* wsum = offs + E + 1;         // [NT / 64]
+  const int A = T * kt, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int e = threadIdx.x; e < E; e += NT) rows[e] = 0u;
+  __syncthreads();
+  for (int a = threadIdx.x; a < A; a += NT) {
+    const int id = ids[a];
+    if (id >= 0 && id < E) atomicOr(&rows[id], 1u << (a / kt));
+  }
+  __syncthreads();
+  int carry = 0;  // total of the earlier chunks of experts
+  for (int e0 = 0; e0 <= E; e0 += NT) {
+    const int e = e0 + threadIdx.x;
+    const int c = e < E ? __builtin_popcount(rows[e]) : 0;
+    const int incl = wave_prefix_sum(c);
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int before = carry, chunk = 0;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) {
+      const int v = wsum[w];
+      before += w < wave ? v : 0;
+      chunk += v;
+    }
+    if (e <= E) {
+      offs[e] = before + incl - c;
+      offsets[e] = before + incl - c;
+    }
+    carry += chunk;
+    __syncthreads();  // offs complete; wsum free for the next chunk
+  }
+  for (int a = threadIdx.x; a < A; a += NT) {
+    const int id = ids[a];
+    if (id >= 0 && id < E) {
+      const int pos = offs[id] + __builtin_popcount(rows[id] & ((1u << (a / kt)) - 1u));
+      perm[pos] = (int32_t)a;
+      inv[a] = pos;
+    } else {
+      inv[a] = -1;
+    }
+  }
+  for (int i = offs[E] + threadIdx.x; i < A; i += NT) perm[i] = -1;
+}
+
 // waves of a permute_block over A assignments and E experts with `lds_ints`
 // ints of LDS for hist: one per 64 assignments (more would only add empty
 // histograms to clear and scan), at most max_waves and what the LDS holds

@@ -158,7 +158,8 @@ __global__ __launch_bounds__(kRouteBlock) void topk_kernel(RouteParams P) {
 // up to 16 rows.  The block that completes last (a device-scope counter in
 // the workspace decides) gives one wave to each row: the wave sums that row's
 // split-K partials in order (as final_logit does), takes its top-k and
-// writes ids/p; the block then sorts the assignments.  Partials are written
+// writes ids/p; the block then sorts the assignments (by the rows' expert
+// masks, since a row names an expert at most once).  Partials are written
 // through and read past L2 (store_coherent/load_coherent) and each thread
 // drains its stores before the block's counter increment, so no device-wide
 // fence (an L2 write-back plus invalidate per wave) is needed.  The finishing
@@ -170,6 +171,7 @@ struct RouteDecodeParams {
   int32_t* perm;       // [T * kt]
   int32_t* inv;        // [T * kt]
   int E_total, W, nbits;
+  int rows_fit;  // permute_rows' LDS fits (else the counting sorts)
 };
 
 constexpr int kDecodeLdsInts = 8192;  // LDS ints of the fused kernel (32 KiB)
@@ -205,7 +207,9 @@ __global__ __launch_bounds__(kGemvBlock) void route_decode_kernel(RouteDecodePar
   }
   __syncthreads();
   int* hist = (int*)smem + ((A + 63) & ~63);
-  if (A <= kGemvBlock)
+  if (D.rows_fit)
+    permute_rows<kGemvBlock>(ids_l, P.T, kt, D.E_total, D.offsets, D.perm, D.inv, hist);
+  else if (A <= kGemvBlock)
     permute_small<kGemvBlock>(ids_l, A, D.E_total, D.offsets, D.perm, D.inv, hist);
   else
     permute_block<kGemvBlock>(ids_l, A, D.E_total, D.W, D.nbits, D.offsets, D.perm, D.inv,
@@ -342,8 +346,9 @@ static int route_decode_impl(const char* who, const void* x, int x_dtype, int T,
   D.E_total = E_total;
   D.W = permute_waves(A, E_total, hist_ints, kGemvBlock / 64);
   D.nbits = id_bits(E_total);
+  D.rows_fit = hist_ints >= 2 * E_total + 1 + kGemvBlock / 64;
   const dim3 grid((E + kGemvExperts - 1) / kGemvExperts, D.r.KS);
-  const size_t lds = (size_t)kDecodeLdsInts * 4;
+  const size_t lds = std::max((size_t)kDecodeLdsInts * 4, (size_t)T * D.r.ks_len * 4);
   hipStream_t s = (hipStream_t)stream;
   if (clear_ctr) {
     const int st = QMOE_LAUNCH("zero_words", zero_words_kernel, dim3(1), 64, 0, s, D.ctr,

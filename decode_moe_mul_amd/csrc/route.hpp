@@ -182,35 +182,87 @@ QMOE_D uint32_t order_key(float f) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-// Top-k of one row of E logits held by one wave (lane l holds experts
-// l + 64 i in raw[i]): k rounds of a wave arg-max (DPP max of the keys, then
-// DPP min of the ids that hold it, so ties go to the lower id).  Lane s < k
-// gets the s-th id and its logit.
-template <int PER>  // E <= 64 * PER
+// The lane's PER (key, slot) pairs sorted by key descending, equal keys by
+// slot ascending: Batcher's odd-even merge network on 64-bit values
+// key << 32 | ~slot, which are all distinct, so the order is unique.
+template <int PER>
+QMOE_D void lane_sort(const uint32_t (&key)[PER], uint32_t (&kk)[PER], uint32_t (&ss)[PER]) {
+  uint64_t v[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) v[i] = ((uint64_t)key[i] << 32) | (uint32_t)~i;
+#pragma unroll
+  for (int p = 1; p < PER; p *= 2)
+#pragma unroll
+    for (int q = p; q >= 1; q /= 2)
+#pragma unroll
+      for (int j = q % p; j + q < PER; j += 2 * q)
+#pragma unroll
+        for (int i = 0; i < q; ++i) {
+          const int a = i + j, b = i + j + q;
+          if (a / (2 * p) == b / (2 * p)) {
+            // bitwise blends, not selects of array elements: the compiler
+            // would turn those into dynamically indexed register arrays
+            const uint64_t m = 0ull - (uint64_t)(v[b] > v[a]);
+            const uint64_t va = v[a], vb = v[b];
+            v[a] = (vb & m) | (va & ~m);
+            v[b] = (va & m) | (vb & ~m);
+          }
+        }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    kk[i] = (uint32_t)(v[i] >> 32);
+    ss[i] = ~(uint32_t)v[i];
+  }
+}
+
+// Top-k of one row of E logits held by one wave (lane l holds expert
+// l + 64 i in raw[i], E <= 64 * PER, PER a power of two).  Each lane sorts
+// its keys once (order key: NaN ranks as -inf; absent experts 0).  A round
+// takes the wave max of the lanes' leading keys; when one lane holds it
+// (the common case, found with one ballot) that lane wins, otherwise a DPP
+// min over slot * 64 + lane picks the lowest id among the tied lanes (a
+// lane's equal keys are in slot order).  The winner drops its leading key.
+// Lane s < k gets the s-th id and its logit (read from the owning lane at
+// the end).
+template <int PER>
 QMOE_D void wave_topk(const float (&raw)[PER], int E, int k, int& my_id, float& my_raw) {
+  static_assert((PER & (PER - 1)) == 0, "PER must be a power of two");
   const int lane = threadIdx.x & 63;
-  uint32_t key[PER];
+  uint32_t key[PER], kk[PER], ss[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) key[i] = lane + 64 * i < E ? order_key(raw[i]) : 0u;
-  my_id = 0;
-  my_raw = 0.f;
+  lane_sort<PER>(key, kk, ss);
+  int src_lane = 0, src_slot = 0;
   for (int s = 0; s < k; ++s) {
-    uint32_t kb = 0u, ib = 0xFFFFFFFFu;
-    float rb = 0.f;
-#pragma unroll
-    for (int i = 0; i < PER; ++i)  // ascending ids, strict: lowest id on ties
-      if (key[i] > kb) { kb = key[i]; ib = (uint32_t)(lane + 64 * i); rb = raw[i]; }
-    const uint32_t kmax = wave_max_u32(kb);
-    const uint32_t wid = wave_min_u32(kb == kmax ? ib : 0xFFFFFFFFu);
-    const float rsel = __builtin_bit_cast(
-        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rb), (int)(wid & 63u)));
-    if ((int)(wid & 63u) == lane) {
-#pragma unroll
-      for (int i = 0; i < PER; ++i)
-        if (i == (int)(wid >> 6)) key[i] = 0u;
+    const uint32_t kmax = wave_max_u32(kk[0]);  // > 0 while s < k <= E
+    const uint64_t m = __builtin_amdgcn_ballot_w64(kk[0] == kmax);
+    int wl, ws;
+    if (__builtin_popcountll(m) == 1) {
+      wl = (int)__builtin_ctzll(m);
+      ws = __builtin_amdgcn_readlane((int)ss[0], wl);
+    } else {
+      const uint32_t wid =
+          wave_min_u32(kk[0] == kmax ? ss[0] * 64u + (uint32_t)lane : 0xFFFFFFFFu);
+      wl = (int)(wid & 63u);
+      ws = (int)(wid >> 6);
     }
-    if (lane == s) { my_id = (int)wid; my_raw = rsel; }
+    if (lane == s) { src_lane = wl; src_slot = ws; }
+    const uint32_t w = lane == wl ? ~0u : 0u;  // the winner shifts its list
+#pragma unroll
+    for (int i = 0; i + 1 < PER; ++i) {
+      kk[i] = (kk[i + 1] & w) | (kk[i] & ~w);
+      ss[i] = (ss[i + 1] & w) | (ss[i] & ~w);
+    }
+    kk[PER - 1] &= ~w;
   }
+  float g = 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const float v = __shfl(raw[i], src_lane, 64);
+    g = i == src_slot ? v : g;
+  }
+  my_id = lane < k ? src_slot * 64 + src_lane : 0;
+  my_raw = lane < k ? g : 0.f;
 }
 
 // ids/p of row t from its top-k (softmax over the kept logits relative to
@@ -268,9 +320,10 @@ QMOE_D void row_logits(const RouteParams& P, int t, float (&v)[PER]) {
 
 inline void route_split(int T, int H, int& KS, int& ks_len) {
   if (T > kGemvRowsMax) { KS = 1; ks_len = H; return; }
-  // K-slices of 1024 values (multiple of 256), capped so T*ks_len*4 <= 32 KiB
+  // K-slices of 1024 values (multiple of 256), capped so T*ks_len*4 <= 64 KiB
+  // (the staged slice of every row fits a block's default LDS limit)
   ks_len = 1024;
-  while (ks_len > 256 && (size_t)T * ks_len * 4 > 32768) ks_len /= 2;
+  while (ks_len > 256 && (size_t)T * ks_len * 4 > 65536) ks_len /= 2;
   KS = (H + ks_len - 1) / ks_len;
 }
 
