@@ -820,7 +820,24 @@ QMOE_D int scheduled_expert(const int32_t* offsets, int E, int m_max, int b, int
   const int per = (E + kBlock - 1) / kBlock;
   const int lo = min(E, tid * per), hi = min(E, lo + per);
   int nb = 0, ns = 0;
-  {
+  // Up to kKeep experts per thread (E <= 1024): the thread's offsets stay in
+  // registers for the lookup below, which then needs no second memory round
+  // trip.  All kKeep + 1 loads are unconditional (clamped to offsets[E]).
+  constexpr int kKeep = 4;
+  const bool keep = per <= kKeep;  // block-uniform
+  int ov[kKeep + 1];
+  if (keep) {
+#pragma unroll
+    for (int j = 0; j <= kKeep; ++j) ov[j] = offsets[min(lo + j, E)];
+#pragma unroll
+    for (int j = 0; j < kKeep; ++j) {
+      const int m = ov[j + 1] - ov[j];
+      if (lo + j < hi) {
+        nb += m > m_max;
+        ns += m > 0 && m <= m_max;
+      }
+    }
+  } else {
     int prev = lo < hi ? offsets[lo] : 0;
     for (int e0 = lo; e0 < hi; e0 += 4) {
       int nx[4];
@@ -866,16 +883,31 @@ QMOE_D int scheduled_expert(const int32_t* offsets, int E, int m_max, int b, int
   const int first = big ? xb : xs, count = big ? nb : ns;
   if ((big || want < ts) && want >= first && want < first + count) {
     int c = first;
-    for (int e = lo; e < hi; ++e) {
-      const int p0 = offsets[e], m = offsets[e + 1] - p0;
-      if (big ? m > m_max : (m > 0 && m <= m_max)) {
-        if (c == want) {
-          red[2 * kWaves] = e;
-          red[2 * kWaves + 1] = p0;
-          red[2 * kWaves + 2] = m;
-          break;
+    if (keep) {
+#pragma unroll
+      for (int j = 0; j < kKeep; ++j) {
+        const int p0 = ov[j], m = ov[j + 1] - p0;
+        if (lo + j < hi && (big ? m > m_max : (m > 0 && m <= m_max))) {
+          if (c == want) {
+            red[2 * kWaves] = lo + j;
+            red[2 * kWaves + 1] = p0;
+            red[2 * kWaves + 2] = m;
+          }
+          ++c;
         }
-        ++c;
+      }
+    } else {
+      for (int e = lo; e < hi; ++e) {
+        const int p0 = offsets[e], m = offsets[e + 1] - p0;
+        if (big ? m > m_max : (m > 0 && m <= m_max)) {
+          if (c == want) {
+            red[2 * kWaves] = e;
+            red[2 * kWaves + 1] = p0;
+            red[2 * kWaves + 2] = m;
+            break;
+          }
+          ++c;
+        }
       }
     }
   }
