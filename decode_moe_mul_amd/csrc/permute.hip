@@ -11,6 +11,9 @@ namespace qmoe {
 
 constexpr int kPermBlock = 1024;
 constexpr int kPermLds = 15872;  // ints of LDS for hist/cursors (62 KiB)
+// 64-chunks of ids a wave loads at once: 24 cover a 2048-row chunk's 20480
+// top-10 assignments over 16 waves, so each wave reads its ids once.
+constexpr int kPermIdBatch = 24;
 
 __global__ __launch_bounds__(kPermBlock) void permute_kernel(const int32_t* ids, int A, int E,
                                                              int W, int nbits,
@@ -18,7 +21,7 @@ __global__ __launch_bounds__(kPermBlock) void permute_kernel(const int32_t* ids,
                                                              int32_t* inv) {
   __shared__ int hist[kPermLds];  // [W][E]
   __shared__ int wsum[kPermBlock / 64];
-  permute_block<kPermBlock>(ids, A, E, W, nbits, offsets, perm, inv, hist, wsum);
+  permute_block<kPermBlock, kPermIdBatch>(ids, A, E, W, nbits, offsets, perm, inv, hist, wsum);
 }
 
 }  // namespace qmoe

@@ -29,18 +29,18 @@ QMOE_D uint64_t peers_of(int id, int nbits, uint64_t active) {
 }
 
 // NT threads; hist holds W*E ints and wsum NT/64 ints of LDS.  ids may live
-// in global memory or LDS.  Called by every thread of the block.
-template <int NT>
+// in global memory or LDS.  Called by every thread of the block.  The ids of
+// kIdBatch 64-chunks are loaded together (every lane loads; past the range it
+// re-reads the range's last id), so a pass waits for memory once per batch
+// rather than once per chunk; a wave whose range fits one batch loads it once
+// for both passes.
+template <int NT, int kIdBatch = 8>
 QMOE_D void permute_block(const int32_t* ids, int A, int E, int W, int nbits, int32_t* offsets,
                           int32_t* perm, int32_t* inv, int* hist, int* wsum) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int i = threadIdx.x; i < W * E; i += NT) hist[i] = 0;
   __syncthreads();
   const long long a_begin = (long long)wave * A / W, a_end = (long long)(wave + 1) * A / W;
-  // The ids of kIdBatch 64-chunks are loaded together (every lane loads; past
-  // the range it re-reads the range's last id), so a pass waits for memory
-  // once per batch rather than once per chunk.
-  constexpr int kIdBatch = 8;
   auto load_batch = [&](long long c0, int (&idb)[kIdBatch]) {
 #pragma unroll
     for (int j = 0; j < kIdBatch; ++j) {
@@ -48,11 +48,19 @@ QMOE_D void permute_block(const int32_t* ids, int A, int E, int W, int nbits, in
       idb[j] = ids[a < a_end ? a : a_end - 1];
     }
   };
+  const bool once = a_end - a_begin <= 64 * kIdBatch;  // wave-uniform
+  int idk[kIdBatch];
+  if (wave < W && a_begin < a_end && once) load_batch(a_begin, idk);
   // pass 1: per-wave histogram
   if (wave < W && a_begin < a_end) {
     for (long long c0 = a_begin; c0 < a_end; c0 += 64 * kIdBatch) {
       int idb[kIdBatch];
-      load_batch(c0, idb);
+      if (once) {
+#pragma unroll
+        for (int j = 0; j < kIdBatch; ++j) idb[j] = idk[j];
+      } else {
+        load_batch(c0, idb);
+      }
 #pragma unroll
       for (int j = 0; j < kIdBatch; ++j) {
         const long long c = c0 + 64 * j;
@@ -102,7 +110,12 @@ QMOE_D void permute_block(const int32_t* ids, int A, int E, int W, int nbits, in
   if (wave < W && a_begin < a_end) {
     for (long long c0 = a_begin; c0 < a_end; c0 += 64 * kIdBatch) {
       int idb[kIdBatch];
-      load_batch(c0, idb);
+      if (once) {
+#pragma unroll
+        for (int j = 0; j < kIdBatch; ++j) idb[j] = idk[j];
+      } else {
+        load_batch(c0, idb);
+      }
 #pragma unroll
       for (int j = 0; j < kIdBatch; ++j) {
         const long long c = c0 + 64 * j;
