@@ -42,26 +42,26 @@ QMOE_D float4 load_act4(const void* x, size_t i) {
   }
 }
 
-// x[:, k0:k0+len] -> xsl [T][ks_len], float4 granules, 4 loads in flight
+// x[:, k0:k0+len] -> xsl [T][ks_len], float4 granules, 4 loads in flight.
+// Loads and stores are unconditional: a granule index past the end is
+// clamped to the last granule, whose value it then writes again.  (With the
+// stores under a condition the compiler moves each load into its store's
+// branch, and the loads no longer fly together.)
 template <int DT, int NT>
 QMOE_D void stage_x_slice(const RouteParams& P, int k0, int len, float* xsl) {
   const int l4 = len >> 2, n4 = P.T * l4;
   for (int i0 = threadIdx.x; i0 < n4; i0 += 4 * NT) {
     float4 v[4];
+    int at[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int i = min(i0 + u * NT, n4 - 1);  // unconditional loads
+      const int i = min(i0 + u * NT, n4 - 1);
       const int t = i / l4, j = 4 * (i - t * l4);
       v[u] = load_act4<DT>(P.x, (size_t)t * P.H + k0 + j);
+      at[u] = t * P.ks_len + j;
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = i0 + u * NT;
-      if (i < n4) {
-        const int t = i / l4, j = 4 * (i - t * l4);
-        *(float4*)(xsl + t * P.ks_len + j) = v[u];
-      }
-    }
+    for (int u = 0; u < 4; ++u) *(float4*)(xsl + at[u]) = v[u];
   }
 }
 
