@@ -103,6 +103,26 @@ def test_route_exact_ties_go_to_lower_id():
             assert 7 in row and row.index(7) < row.index(40)
 
 
+@pytest.mark.parametrize("T,E,k,period", [(6, 512, 10, 64), (6, 512, 10, 32), (16, 256, 9, 16),
+                                           (3, 300, 12, 64), (2, 512, 64, 8)])
+def test_route_ties_within_and_across_lanes(T, E, k, period):
+    """Experts e and e + period share a router row, so their logits are exactly
+    equal: with period 64 every lane of the top-k wave holds equal keys in all
+    its slots (ties within a lane), with 32, 16 or 8 also across lanes.  Both
+    the chunk path (moe_route) and the fused decode routing must pick the
+    top k by logit with ties to the lower id, in that order."""
+    H = 256
+    x = synth.normal((T, H), 1.0, 21, synth.ACT, T)
+    base = synth.normal((period, H), 0.02, 21, synth.ROUTER)
+    Wr = np.ascontiguousarray(base[np.arange(E) % period])
+    ids, p, lg = qmoe.route(to_gpu(x), to_gpu(Wr), None, k, logits=True)
+    ids, lg = to_np(ids), to_np(lg)
+    assert (lg[:, :period] == lg[:, period:2 * period]).all()
+    _check_topk_property(lg, ids, k)
+    got = _route_decode_vs_two_calls(to_gpu(x), to_gpu(Wr), None, k)
+    _check_topk_property(to_np(got[5]), to_np(got[0]), k)
+
+
 def test_route_k1_weights_are_one():
     x = synth.normal((5, 512), 1.0, 4, synth.ACT)
     Wr = synth.normal((16, 512), 0.02, 4, synth.ROUTER)
