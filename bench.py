@@ -31,8 +31,9 @@ Timed passes (each over the same steps, inputs and weight rotation):
      launch each: one_launch_layer (context only).
 Also reported: per row count the weight bytes, GB/s and fraction of the 8 TB/s
 HBM peak; the gate/up HBM traffic from stored counter runs; a plain streaming
-read (the part's ceiling, and its rate at the workloads' sizes) and the floor
-of a dependent launch; the CPU oracle timed on a bounded sample of every
+read (the part's ceiling, and its rate at the workloads' sizes), the floor
+of a dependent launch and one wave's dependent-step latencies (with the cost of
+the routing's top-k); the CPU oracle timed on a bounded sample of every
 workload; and, outside the step, the dense layer GEMV (Llama-3-8B shapes,
 Q4_K/Q6_K and the ternary T5 format), the 2048-row prefill chunk, the
 block-scaled MX GEMM and the int8 GEMV and GEMM.
@@ -760,6 +761,13 @@ def stream_ceiling(torch, reps=20):
     del g
     log(f"dependent launches: {out['launch_chain_graph_us']} us each in a graph, "
         f"{out['launch_chain_eager_us']} us eager")
+    # one wave's dependent-step latencies and the routing top-k (median of 5)
+    runs = [qmoe.wave_latency() for _ in range(6)][1:]
+    lat = {k: sorted(r[k] for r in runs)[len(runs) // 2] for k in runs[0]}
+    mhz = lat["shader_clock_mhz"] or 2400
+    lat["wave_topk_512_k10_us"] = round(lat["wave_topk_512_k10_cycles"] / mhz, 3)
+    out["wave_latency"] = lat
+    log(f"wave latency: {lat}")
     return out
 
 

@@ -75,6 +75,7 @@ _SIGNATURES = {
     "moe_layer_decode": (_I, [ctypes.POINTER(Tier), _I, _I, _I, _I, _VP, _I, _I, _VP, _VP, _I,
                               _I, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "qmoe_stream_read": (_I, [_VP, _SZ, _I, _VP, _VP]),
+    "qmoe_wave_latency": (_I, [_VP, _VP]),
     "qmoe_profile_enable": (_I, [_I]),
     "qmoe_profile_reset": (_I, []),
     "qmoe_profile_only": (_I, [ctypes.c_char_p]),
@@ -515,6 +516,18 @@ def layer_decode(tiers, E, H, F, x, Wr, bias, k, n_shared=0, out=None, ws=None, 
 
 
 # ------------------------------------------------------------ measurement --
+
+def wave_latency():
+    """qmoe_wave_latency: one wave's dependent-step latencies (shader cycles)
+    and the routing top-k's cost, as a dict."""
+    torch = _torch()
+    out = torch.zeros(8, dtype=torch.int64, device="cuda")
+    _check(lib().qmoe_wave_latency(_p(out), _stream()), "qmoe_wave_latency")
+    v = out.cpu().tolist()
+    return {"valu_dependent_cycles": v[0], "dpp_wave_max_cycles": v[1],
+            "ballot_round_trip_cycles": v[2], "wave_topk_512_k10_cycles": v[3],
+            "lane_sort_8_cycles": v[4], "shader_clock_mhz": v[5]}
+
 
 def stream_read(buf, blocks_per_cu=8, sink=None):
     """One streaming read of the CUDA tensor buf (qmoe_stream_read)."""

@@ -430,6 +430,17 @@ int moe_layer_decode(const qmoe_tier *tiers, int n_tiers, int E, int H, int F,
 int qmoe_stream_read(const void *buf, size_t bytes, int blocks_per_cu,
                      uint32_t *sink, void *stream);
 
+/* qmoe_wave_latency: runs one 64-lane wave that times, with the shader clock,
+ * the dependent steps a single wave per routed row works through in the decode
+ * routing's tail (the top-k of [P2] "瓶颈分析": 10 of 512 experts per token):
+ *   out[0] cycles per dependent vector op, out[1] per DPP wave max with its
+ *   read-back to a scalar, out[2] per ballot round trip (compare, ballot,
+ *   first set lane, read-lane), out[3] per top-k of 512 keys with k = 10 (the
+ *   library's own wave top-k), out[4] per sort of a lane's 8 keys, out[5] the
+ *   shader clock in MHz over the run, out[6] a value without meaning.
+ * out: 8 device words (uint64), written by one thread.  For measurement only. */
+int qmoe_wave_latency(uint64_t *out, void *stream);
+
 /* ----------------------------------------------------------- profiling --
  * Optional per-kernel timing with HIP events recorded around every launch the
  * library makes while enabled (on the launch stream).  qmoe_profile_read

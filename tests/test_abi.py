@@ -228,6 +228,8 @@ def test_newer_entry_points_validate_on_the_host(L):
     assert L.qgemm_q8_0_i8(None, 64, 64, fake, fake, 16, fake, None) == -1
     assert L.qgemm_q8_0_i8(ctypes.c_void_p(256 * 1000 + 16), 64, 64, fake, fake, 16, fake,
                            None) == -1                                          # W misaligned
+    # qmoe_wave_latency: its output pointer
+    assert L.qmoe_wave_latency(None, None) == -1
     # qmoe_stream_read: sizes, alignment, blocks per CU
     assert L.qmoe_stream_read(fake, 0, 8, fake, None) == 0
     assert L.qmoe_stream_read(fake, 24, 8, fake, None) == -1
