@@ -13,6 +13,7 @@
 //  topk_kernel         one wave per row: sums the split-K partials in fixed
 //                      order, adds the bias, selects k by repeated wave
 //                      arg-max, softmax over the kept logits.
+#include <algorithm>
 #include <mutex>
 
 #include "route.hpp"
@@ -24,21 +25,24 @@ __global__ __launch_bounds__(kGemvBlock) void router_gemv_kernel(RouteParams P) 
   router_partials<false, kGemvBlock>(P, xsl, blockIdx.x, blockIdx.y);
 }
 
-// 64 x 64 tile of logits (rows x experts) on the matrix cores in fp32
-// (v_mfma_f32_16x16x4_f32, fp32 products and sums).  Wave w computes rows
-// 32 (w >> 1) .. and experts 32 (w & 1) .. of the tile as 2 x 2 blocks of
-// 16 x 16.  Per 16-wide chunk of H each lane loads 4 consecutive values of
-// its row of x and of its expert's row of Wr; op s of the chunk takes value s
-// of every lane group, so both operands walk the chunk's 16 indices in the
-// same interleaved order.  Four chunks of loads are in flight.
-constexpr int kGT = 64, kGE = 64, kGDepth = 4;
+// 128 x 128 tile of logits (rows x experts) over one K slice on the matrix
+// cores in fp32 (v_mfma_f32_16x16x4_f32, fp32 products and sums).  Wave w
+// computes rows 64 (w >> 1) .. and experts 64 (w & 1) .. of the tile as
+// 4 x 4 blocks of 16 x 16, so each operand value a lane loads feeds four
+// blocks (with 2 x 2 blocks per wave the operand loads, not the matrix cores,
+// bounded the kernel).  Per 16-wide chunk of the slice each lane loads 4
+// consecutive values of its rows of x and of its experts' rows of Wr; op s of
+// the chunk takes value s of every lane group, so both operands walk the
+// chunk's 16 indices in the same interleaved order.  Two chunks of loads are
+// in flight.  Slice blockIdx.z writes part[z][t][e].
+constexpr int kGT = 128, kGE = 128, kGDepth = 2;
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 template <int DT>
-QMOE_D void rg_load(const RouteParams& P, const int (&trow)[2], const int (&erow)[2], int k,
-                    float4 (&a)[2], float4 (&b)[2]) {
+QMOE_D void rg_load(const RouteParams& P, const int (&trow)[4], const int (&erow)[4], int k,
+                    float4 (&a)[4], float4 (&b)[4]) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < 4; ++i) {
     a[i] = load_act4<DT>(P.x, (size_t)trow[i] * P.H + k);
     b[i] = *(const float4*)(P.Wr + (size_t)erow[i] * P.H + k);
   }
@@ -48,42 +52,44 @@ template <int DT>
 __global__ __launch_bounds__(kRouteBlock) void router_gemm_kernel(RouteParams P) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, kg = lane >> 4;
-  const int tb = blockIdx.y * kGT + 32 * (wave >> 1), eb = blockIdx.x * kGE + 32 * (wave & 1);
+  const int tb = blockIdx.y * kGT + 64 * (wave >> 1), eb = blockIdx.x * kGE + 64 * (wave & 1);
   // operand rows, clamped: rows past the end re-read the last one (dropped)
-  int trow[2], erow[2];
+  int trow[4], erow[4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < 4; ++i) {
     trow[i] = min(tb + 16 * i + r, P.T - 1);
     erow[i] = min(eb + 16 * i + r, P.E - 1);
   }
-  const int nch = (P.H + 15) / 16;
-  // this lane's 4 values of chunk c start at k; past H (when H % 16 != 0)
-  // the load re-reads the last 4 and the values are zeroed
-  auto k_of = [&](int c) { return min(16 * c + 4 * kg, P.H - 4); };
-  f32x4_t acc[2][2];
+  const int k0 = blockIdx.z * P.ks_len, klen = min(P.ks_len, P.H - k0);  // klen % 4 == 0
+  const int nch = (klen + 15) / 16;
+  // this lane's 4 values of chunk c start at k; past the slice (when its
+  // length is not a multiple of 16) the load re-reads the last 4 and the
+  // values are zeroed
+  auto k_of = [&](int c) { return k0 + min(16 * c + 4 * kg, klen - 4); };
+  f32x4_t acc[4][4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float4 ra[kGDepth][2], rb[kGDepth][2];
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float4 ra[kGDepth][4], rb[kGDepth][4];
 #pragma unroll
   for (int u = 0; u < kGDepth; ++u) rg_load<DT>(P, trow, erow, k_of(min(u, nch - 1)), ra[u], rb[u]);
   for (int c0 = 0; c0 < nch; c0 += kGDepth) {
 #pragma unroll
     for (int u = 0; u < kGDepth; ++u) {
       const int c = c0 + u;
-      const bool valid = c < nch && 16 * c + 4 * kg < P.H;
-      float4 a[2], b[2];
+      const bool valid = c < nch && 16 * c + 4 * kg < klen;
+      float4 a[4], b[4];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < 4; ++i) {
         a[i] = valid ? ra[u][i] : make_float4(0.f, 0.f, 0.f, 0.f);
         b[i] = rb[u][i];
       }
       rg_load<DT>(P, trow, erow, k_of(min(c + kGDepth, nch - 1)), ra[u], rb[u]);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < 4; ++j) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i].x, b[j].x, acc[i][j], 0, 0, 0);
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i].y, b[j].y, acc[i][j], 0, 0, 0);
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i].z, b[j].z, acc[i][j], 0, 0, 0);
@@ -92,15 +98,33 @@ __global__ __launch_bounds__(kRouteBlock) void router_gemm_kernel(RouteParams P)
     }
   }
   // lane holds rows 4 kg + q of each 16 x 16 block, column r
+  float* part = P.part + (size_t)blockIdx.z * P.T * P.E;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int t = tb + 16 * i + 4 * kg + q, e = eb + 16 * j + r;
-        if (t < P.T && e < P.E) P.part[(size_t)t * P.E + e] = acc[i][j][q];
+        if (t < P.T && e < P.E) part[(size_t)t * P.E + e] = acc[i][j][q];
       }
+}
+
+// K split of the matrix-core router (more than kGemvRowsMax rows): slices of
+// whole 16-value chunks, as many as bring the launch to about 256 blocks of
+// 128 x 128 tiles (at most 8).
+static void gemm_split(int T, int H, int E, int& KS, int& ks_len) {
+  const long long tiles = (long long)((E + kGE - 1) / kGE) * ((T + kGT - 1) / kGT);
+  const int want = (int)std::max<long long>(1, std::min<long long>(8, (256 + tiles - 1) / tiles));
+  ks_len = ((H + want - 1) / want + 15) / 16 * 16;
+  KS = (H + ks_len - 1) / ks_len;
+}
+
+// The router's K split for T rows: route_split up to kGemvRowsMax rows, the
+// matrix-core split beyond.
+static void router_split(int T, int H, int E, int& KS, int& ks_len) {
+  if (T > kGemvRowsMax) gemm_split(T, H, E, KS, ks_len);
+  else route_split(T, H, KS, ks_len);
 }
 
 
@@ -227,7 +251,7 @@ extern "C" {
 size_t moe_route_workspace_size(int T, int H, int E) {
   if (T < 0 || H <= 0 || E <= 0) return 0;
   int KS, ks_len;
-  route_split(T, H, KS, ks_len);
+  router_split(T, H, E, KS, ks_len);
   return round_up256((size_t)KS * T * E * sizeof(float)) + 256;
 }
 
@@ -250,7 +274,7 @@ int moe_route(const void* x, int x_dtype, int T, int H, const float* Wr, const f
     return fail(QMOE_ERR_WORKSPACE, "moe_route: workspace %zu < %zu (or misaligned)", ws_bytes,
                 need);
   RouteParams P{x, x_dtype, T, H, Wr, bias, E, k, n_shared, ids, p, logits, (float*)ws, 0, 0};
-  route_split(T, H, P.KS, P.ks_len);
+  router_split(T, H, E, P.KS, P.ks_len);
   hipStream_t s = (hipStream_t)stream;
   int st;
   if (T <= kGemvRowsMax) {
@@ -258,7 +282,7 @@ int moe_route(const void* x, int x_dtype, int T, int H, const float* Wr, const f
     st = QMOE_LAUNCH("router_gemv", router_gemv_kernel, grid, kGemvBlock,
                      (size_t)T * P.ks_len * sizeof(float), s, P);
   } else {
-    const dim3 grid((E + kGE - 1) / kGE, (T + kGT - 1) / kGT);
+    const dim3 grid((E + kGE - 1) / kGE, (T + kGT - 1) / kGT, P.KS);
     st = x_dtype == QMOE_F32
              ? QMOE_LAUNCH("router_gemm", router_gemm_kernel<QMOE_F32>, grid, kRouteBlock, 0, s, P)
              : QMOE_LAUNCH("router_gemm", router_gemm_kernel<QMOE_BF16>, grid, kRouteBlock, 0, s, P);
