@@ -128,49 +128,21 @@ static void router_split(int T, int H, int E, int& KS, int& ks_len) {
 }
 
 
-// Final logits of row t, expert e: split-K partials summed in order + bias.
-QMOE_D float final_logit(const RouteParams& P, int t, int e) {
-  float v = 0.f;
-  for (int s0 = 0; s0 < P.KS; s0 += 8) {
-    float pv[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      pv[u] = s0 + u < P.KS
-                  ? P.part[((size_t)(s0 + u) * P.T + t) * P.E + e]
-                  : 0.f;
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (s0 + u < P.KS) v += pv[u];
-  }
-  if (P.bias) v += P.bias[e];
-  return v;
-}
-
+// One wave per row: the row's final logits (split-K partials summed in slice
+// order, then the bias: row_logits, whose loads for all the lane's experts
+// are in flight together), then its top-k.
 template <int PER>  // values per lane: E <= 64 * PER
 __global__ __launch_bounds__(kRouteBlock) void topk_kernel(RouteParams P) {
-  __shared__ float row[4][64 * PER];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wave;
   if (t >= P.T) return;
-  constexpr int C = PER < 8 ? PER : 8;  // experts per lane whose loads fly together
-#pragma unroll
-  for (int i0 = 0; i0 < PER; i0 += C) {
-    float v[C];
-#pragma unroll
-    for (int i = 0; i < C; ++i) v[i] = final_logit(P, t, min(lane + 64 * (i0 + i), P.E - 1));
-#pragma unroll
-    for (int i = 0; i < C; ++i) {
-      const int e = lane + 64 * (i0 + i);
-      if (e < P.E) {
-        row[wave][e] = v[i];
-        if (P.logits) P.logits[(size_t)t * P.E + e] = v[i];
-      }
-    }
-  }
-  __builtin_amdgcn_wave_barrier();
   float raw[PER];
+  row_logits<PER>(P, t, raw);
+  if (P.logits) {
 #pragma unroll
-  for (int i = 0; i < PER; ++i) raw[i] = lane + 64 * i < P.E ? row[wave][lane + 64 * i] : 0.f;
+    for (int i = 0; i < PER; ++i)
+      if (lane + 64 * i < P.E) P.logits[(size_t)t * P.E + lane + 64 * i] = raw[i];
+  }
   int my_id;
   float my_raw;
   wave_topk<PER>(raw, P.E, P.k, my_id, my_raw);
@@ -181,7 +153,7 @@ __global__ __launch_bounds__(kRouteBlock) void topk_kernel(RouteParams P) {
 // router_partials -> final logits -> top-k -> permutation in one launch for
 // up to 16 rows.  The block that completes last (a device-scope counter in
 // the workspace decides) gives one wave to each row: the wave sums that row's
-// split-K partials in order (as final_logit does), takes its top-k and
+// split-K partials in slice order (as moe_route's top-k does), takes its top-k and
 // writes ids/p; the block then sorts the assignments (by the rows' expert
 // masks, since a row names an expert at most once).  Partials are written
 // through and read past L2 (store_coherent/load_coherent) and each thread

@@ -286,9 +286,10 @@ QMOE_D void write_topk(const RouteParams& P, int t, int my_id, float my_raw, int
   }
 }
 // Final logits of row t for the lane's experts e = lane + 64 i: the KS
-// partials summed in slice order, then the bias (final_logit's order, so the
-// values equal moe_route's bit for bit).  Up to 32 loads per lane in flight;
-// row and slice offsets are wave-uniform (scalar), expert offsets per lane.
+// partials summed in slice order, then the bias (moe_route's top-k kernel and
+// the fused decode routing both take their logits from here, so they agree
+// bit for bit).  Up to 32 loads per lane in flight; row and slice offsets are
+// wave-uniform (scalar), expert offsets per lane.
 template <int PER>
 QMOE_D void row_logits(const RouteParams& P, int t, float (&v)[PER]) {
   constexpr int SC = PER >= 16 ? 1 : 32 / PER;  // K-slices per batch of loads
