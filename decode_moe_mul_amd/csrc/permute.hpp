@@ -2,8 +2,7 @@
 // workgroup: shared by moe_permute and the fused decode routing kernel.
 // Wave w of the first W waves owns the contiguous assignment range
 // [w*A/W, (w+1)*A/W):
-//   pass 1: per-wave histogram hist[w][e] in LDS (lanes with the same id are
-//           found with ballots over the id bits; their leader adds the count);
+//   pass 1: per-wave histogram hist[w][e] in LDS (LDS atomic adds);
 //   scan:   offsets[e] = sum over e' < e, then per-wave cursors
 //           cursor[w][e] = offsets[e] + sum over w' < w of hist[w'][e];
 //   pass 2: each wave walks its range in order and places assignment a at
@@ -66,13 +65,9 @@ QMOE_D void permute_block(const int32_t* ids, int A, int E, int W, int nbits, in
         const long long c = c0 + 64 * j;
         if (c >= a_end) break;  // wave-uniform
         const long long a = c + lane;
-        const bool in = a < a_end;
         const int id = idb[j];
-        const bool valid = in && id >= 0 && id < E;
-        const uint64_t active = __ballot(valid);
-        const uint64_t peers = peers_of(valid ? id : 0, nbits, active);
-        if (valid && (peers & lanes_below(lane)) == 0)
-          hist[wave * E + id] += __popcll(peers);
+        // counts need no order: one LDS atomic per assignment
+        if (a < a_end && id >= 0 && id < E) atomicAdd(&hist[wave * E + id], 1);
       }
     }
   }
