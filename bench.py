@@ -35,8 +35,9 @@ read (the part's ceiling, and its rate at the workloads' sizes), the floor
 of a dependent launch and one wave's dependent-step latencies (with the cost of
 the routing's top-k); the CPU oracle timed on a bounded sample of every
 workload; and, outside the step, the dense layer GEMV (Llama-3-8B shapes,
-Q4_K/Q6_K and the ternary T5 format), the 2048-row prefill chunk, the
-block-scaled MX GEMM and the int8 GEMV and GEMM.
+Q4_K/Q6_K and the ternary T5 format), the 2048-row prefill chunk (also its
+expert GEMMs for the experts of at most 32 rows alone and for the others
+alone), the block-scaled MX GEMM and the int8 GEMV and GEMM.
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--no-cpu-baseline]
                     [--decode-only | --prefill-only] [--one-launch]
@@ -685,6 +686,7 @@ def prefill_chunk(torch, calls=10):
     qmoe.profile_enable(False)
     mx_kern = {k: qmoe.profile_read(k)[1] / calls for k in
                ("prefill_mx_prep", "prefill_gate_up", "prefill_down")}
+    split = _prefill_split(torch, layer, x, ws, calls)
     del layer
     torch.cuda.empty_cache()
     log(f"prefill 2048 rows: {ms:.3f} ms per call (expert GEMMs {gemm_ms:.3f} ms)")
@@ -697,7 +699,59 @@ def prefill_chunk(torch, calls=10):
             "mfma_util_whole_call": round(flops / (ms * 1e-3) / 2.5e15, 4),
             "kernel_ms": {k: round(v, 4) for k, v in kern.items()},
             "mx_tail_tier": {"ms_per_call": round(mx_ms, 4),
-                             "kernel_ms": {k: round(v, 4) for k, v in mx_kern.items()}}}
+                             "kernel_ms": {k: round(v, 4) for k, v in mx_kern.items()}},
+            "by_expert_rows": split}
+
+
+def _prefill_split(torch, layer, x, ws, calls):
+    """The chunk's expert GEMMs (qgemm_grouped_prefill) for two halves of its
+    routing alone: the experts with at most 32 rows (one small tile each,
+    bound by their weight stream) and the others (128-row tiles on the
+    matrix cores).  Each half is the same call with offsets and perm that
+    keep only those experts' rows, so the two times show where the mixed
+    launches' time goes."""
+    from decode_moe_mul_amd import qmoe
+    c = layer.cfg
+    T = x.shape[0]
+    kt = c.k + c.n_shared
+    offs = ws["offsets"].cpu().numpy().astype(np.int64)
+    perm = ws["perm"].cpu().numpy()
+    cnt = np.diff(offs)
+    L = qmoe.lib()
+    s = qmoe._stream()
+    arr = layer.tier_arrays[0]
+    o = torch.empty_like(ws["o"])
+    out = {}
+    for name, keep in (("up_to_32_rows", (cnt > 0) & (cnt <= 32)), ("over_32_rows", cnt > 32)):
+        off2 = np.zeros(c.E_total + 1, np.int32)
+        off2[1:] = np.cumsum(np.where(keep, cnt, 0))
+        rows = np.concatenate([perm[offs[e]:offs[e + 1]] for e in np.nonzero(keep)[0]])
+        p2 = np.zeros(T * kt, np.int32)
+        p2[:len(rows)] = rows
+        off_t = torch.from_numpy(off2).cuda()
+        perm_t = torch.from_numpy(p2).cuda()
+
+        def call(i):
+            qmoe._check(L.qgemm_grouped_prefill(
+                arr, len(arr), c.E_total, c.H, c.F, qmoe._p(x), qmoe._dtype_code(x), T, kt,
+                qmoe._p(off_t), qmoe._p(perm_t), qmoe._p(o), qmoe._p(ws["ffn"]),
+                ws["ffn"].numel(), s), "qgemm_grouped_prefill")
+        for i in range(3):
+            call(i)
+        qmoe.profile_reset()
+        qmoe.profile_enable(True)
+        _events_ms(torch, call, calls)
+        qmoe.profile_enable(False)
+        gu, dn = (qmoe.profile_read(k)[1] / calls for k in ("prefill_gate_up", "prefill_down"))
+        nbytes = sum(layer.expert_bytes(int(e)) for e in np.nonzero(keep)[0])
+        flops = 2.0 * len(rows) * 3 * c.F * c.H
+        out[name] = {"experts": int(keep.sum()), "rows": int(len(rows)),
+                     "weight_bytes": int(nbytes), "gate_up_ms": round(gu, 4),
+                     "down_ms": round(dn, 4),
+                     "weight_gbs": round(nbytes / ((gu + dn) * 1e-3) / 1e9, 1),
+                     "tflops": round(flops / ((gu + dn) * 1e-3) / 1e12, 1)}
+    log(f"prefill split by expert rows: {out}")
+    return out
 
 
 # names of the kernels the library records for one decode layer call
