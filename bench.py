@@ -760,15 +760,16 @@ DECODE_KERNELS = ("route_decode", "router_gemv", "topk", "permute", "ffn_gate_up
 
 
 def stream_ceiling(torch, reps=20):
-    """The HBM read rate of a plain streaming read (qmoe_stream_read: the
-    decode kernels' 16-byte nontemporal loads) over a 2 GiB buffer, best of
-    4 / 8 / 16 blocks per CU: the practical ceiling of a weight stream."""
+    """The HBM read rate of a plain streaming read (qmoe_stream_read: 16-byte
+    nontemporal loads, a contiguous chunk per block, eight loads in flight
+    per lane) over a 2 GiB buffer, best of 2 / 4 / 8 / 16 blocks per CU: the
+    practical ceiling of a weight stream."""
     from decode_moe_mul_amd import qmoe
     nbytes = 2 << 30
     buf = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda").fill_(1)
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     out = {"bytes": nbytes, "per_blocks_per_cu": {}}
-    for bpc in (4, 8, 16):
+    for bpc in (2, 4, 8, 16):
         qmoe.stream_read(buf, bpc, sink)
         ms = _events_ms(torch, lambda i: qmoe.stream_read(buf, bpc, sink), reps)
         out["per_blocks_per_cu"][str(bpc)] = round(nbytes / (ms * 1e-3) / 1e9, 1)
@@ -787,7 +788,7 @@ def stream_ceiling(torch, reps=20):
         for sl in slices:
             qmoe.stream_read(sl, 8, sink)
         best_us = None
-        for bpc in (4, 8, 16):
+        for bpc in (2, 4, 8, 16):
             ms = _events_ms(torch, lambda i: qmoe.stream_read(slices[i % 8], bpc, sink), 40)
             best_us = ms * 1e3 if best_us is None else min(best_us, ms * 1e3)
         out["at_size"][name] = {"bytes": n16, "us": round(best_us, 2),

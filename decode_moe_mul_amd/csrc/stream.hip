@@ -1,10 +1,16 @@
 // qmoe_stream_read: a plain streaming read of a device buffer, for measuring
-// the HBM read rate this part sustains with the decode kernels' access
-// pattern (16-byte nontemporal vector loads, consecutive lanes on
-// consecutive 16-byte chunks, several loads in flight per lane).  Decode is a
+// the HBM read rate this part sustains (16-byte nontemporal vector loads,
+// each block on a contiguous chunk of its own, consecutive lanes on
+// consecutive 16-byte pieces, eight loads in flight per lane).  Decode is a
 // weight stream ([P3] "RTX 3090 Llama 70B three-tier cache" section 4.4:
 // every weight is read once per token), so this rate is the practical
 // ceiling of the decode GEMVs, reported beside the 8 TB/s vendor peak.
+// Of the patterns measured on MI355X over 2 GiB (grid-stride or per-block
+// chunks, 4 or 8 loads per lane, plain or nontemporal, 2 to 16 blocks per
+// CU), per-block chunks with eight nontemporal loads per lane were the
+// fastest and the least sensitive to the block count (6.9 - 7.1 TB/s); a
+// grid-stride read with four loads per lane ranged from 5.8 to 7.0 TB/s
+// with the block count.
 //
 // qmoe_wave_latency: the dependent-issue latencies one wave sees on this part
 // (shader clock cycles), and the cost of the routing's wave top-k on one row,
@@ -15,21 +21,26 @@
 namespace qmoe {
 
 constexpr int kStreamBlock = 256;
-constexpr int kStreamDepth = 4;  // loads in flight per lane
+constexpr int kStreamDepth = 8;  // loads in flight per lane
 
+// Block b reads the b-th of gridDim.x equal chunks, each a whole number of
+// steps of kStreamDepth x 256 x 16 bytes; the remainder past the chunks is
+// read grid-stride, one load per lane at a time.
 __global__ __launch_bounds__(kStreamBlock) void stream_read_kernel(const uint4* p, size_t n16,
                                                                    uint32_t* sink) {
-  const size_t stride = (size_t)gridDim.x * kStreamBlock;
-  size_t i = (size_t)blockIdx.x * kStreamBlock + threadIdx.x;
+  constexpr size_t kStep = (size_t)kStreamDepth * kStreamBlock;
+  const size_t chunk = n16 / gridDim.x / kStep * kStep;
+  const uint4* q = p + (size_t)blockIdx.x * chunk;
   uint32_t acc = 0;
-  for (; i + (kStreamDepth - 1) * stride < n16; i += kStreamDepth * stride) {
+  for (size_t i = threadIdx.x; i < chunk; i += kStep) {
     uint4 v[kStreamDepth];
 #pragma unroll
-    for (int d = 0; d < kStreamDepth; ++d) v[d] = load_stream(p + i + d * stride);
+    for (int d = 0; d < kStreamDepth; ++d) v[d] = load_stream(q + i + d * kStreamBlock);
 #pragma unroll
     for (int d = 0; d < kStreamDepth; ++d) acc ^= v[d].x ^ v[d].y ^ v[d].z ^ v[d].w;
   }
-  for (; i < n16; i += stride) {
+  for (size_t i = chunk * gridDim.x + (size_t)blockIdx.x * kStreamBlock + threadIdx.x; i < n16;
+       i += (size_t)gridDim.x * kStreamBlock) {
     const uint4 v = load_stream(p + i);
     acc ^= v.x ^ v.y ^ v.z ^ v.w;
   }

@@ -419,10 +419,11 @@ int moe_layer_decode(const qmoe_tier *tiers, int n_tiers, int E, int H, int F,
                      void *stream);
 
 /* ------------------------------------------------------- measurement --
- * qmoe_stream_read: reads `bytes` of device memory at buf once, with the
- * decode kernels' access pattern (16-byte nontemporal vector loads,
- * consecutive lanes on consecutive chunks, four loads in flight per lane,
- * blocks_per_cu * CUs blocks of 256 threads), and writes at most one word to
+ * qmoe_stream_read: reads `bytes` of device memory at buf once
+ * (blocks_per_cu * CUs blocks of 256 threads, each block on a contiguous
+ * chunk of its own, 16-byte nontemporal vector loads, consecutive lanes on
+ * consecutive pieces, eight loads in flight per lane; the remainder past the
+ * equal chunks read grid-stride), and writes at most one word to
  * sink[0].  For measuring the HBM read rate the part sustains, the practical
  * ceiling of a weight stream ([P3] section 4.4: decode reads every weight
  * once per token).  buf 16-byte aligned, bytes % 16 == 0, 1 <= blocks_per_cu

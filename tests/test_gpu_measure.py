@@ -8,10 +8,13 @@ from decode_moe_mul_amd import qmoe
 pytestmark = pytest.mark.gpu
 
 
-def test_stream_read_runs_and_writes_at_most_the_sink():
-    buf = torch.arange(1 << 16, dtype=torch.int32, device="cuda")
+@pytest.mark.parametrize("n,bpc", [(1 << 16, 4), ((1 << 23) + 148, 2), ((1 << 23) + 148, 16)])
+def test_stream_read_runs_and_writes_at_most_the_sink(n, bpc):
+    """Sizes below one step per block (all of it read grid-stride) and with
+    whole per-block chunks plus a remainder."""
+    buf = torch.arange(n, dtype=torch.int32, device="cuda")
     sink = torch.zeros(4, dtype=torch.int32, device="cuda")
-    qmoe.stream_read(buf, 4, sink)
+    qmoe.stream_read(buf, bpc, sink)
     torch.cuda.synchronize()
     assert (sink[1:] == 0).all()
 
