@@ -5,12 +5,10 @@
 // weight stream ([P3] "RTX 3090 Llama 70B three-tier cache" section 4.4:
 // every weight is read once per token), so this rate is the practical
 // ceiling of the decode GEMVs, reported beside the 8 TB/s vendor peak.
-// Of the patterns measured on MI355X over 2 GiB (grid-stride or per-block
-// chunks, 4 or 8 loads per lane, plain or nontemporal, 2 to 16 blocks per
-// CU), per-block chunks with eight nontemporal loads per lane were the
-// fastest and the least sensitive to the block count (6.9 - 7.1 TB/s); a
-// grid-stride read with four loads per lane ranged from 5.8 to 7.0 TB/s
-// with the block count.
+// Per-block chunks with eight loads in flight per lane gave the highest rate
+// of the patterns tried on MI355X and varied least with the block count; a
+// grid-stride read with four loads per lane stayed near 6 TB/s at 4 to 16
+// blocks per CU.
 //
 // qmoe_wave_latency: the dependent-issue latencies one wave sees on this part
 // (shader clock cycles), and the cost of the routing's wave top-k on one row,
