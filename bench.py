@@ -27,8 +27,8 @@ Timed passes (each over the same steps, inputs and weight rotation):
      summed kernel time of a call (per_config);
   5. each call captured as a HIP graph and replayed (>= 500 replays,
      median / p10 / p90);
-  6. with --one-launch, the 1- and 6-row calls as one moe_layer_decode
-     launch each: one_launch_layer (context only).
+  6. with --one-launch, each call as one moe_layer_decode launch:
+     one_launch_layer (context only).
 Also reported: per row count the weight bytes, GB/s and fraction of the 8 TB/s
 HBM peak; the gate/up HBM traffic from stored counter runs; a plain streaming
 read (the part's ceiling, and its rate at the workloads' sizes), the floor
@@ -868,7 +868,7 @@ def main():
     ap.add_argument("--prefill-only", action="store_true",
                     help="run only the 2048-row prefill section (prefill counter runs)")
     ap.add_argument("--one-launch", action="store_true",
-                    help="also time the one-launch layer (moe_layer_decode) at 1 and 6 rows")
+                    help="also time the one-launch layer (moe_layer_decode) at 1, 6 and 16 rows")
     ap.add_argument("--graph-iters", type=int, default=500)
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
                     help="print the per-kernel table of a rocprofv3 --kernel-trace run and exit")
@@ -996,13 +996,14 @@ def main():
     one_launch = None
     if a.one_launch:
         one_ms = np.array([timed(one_call(i), f"one launch rows={r}", one_launch=True)
-                           for i, r in enumerate((1, 6))])
+                           for i, r in enumerate(ROWS)])
         for r in (1, 6):
             tiered.check_one_launch(r)
+        grouped.check_one_launch(16)
         one_launch = {"ms_per_call": {str(r): round(one_ms[i] / a.steps, 5)
-                                      for i, r in enumerate((1, 6))},
+                                      for i, r in enumerate(ROWS)},
                       "tokens_per_s": {str(r): round(r * a.steps / (one_ms[i] * 1e-3), 1)
-                                       for i, r in enumerate((1, 6))}}
+                                       for i, r in enumerate(ROWS)}}
 
     per_config = {}
     mean_bytes = call_bytes.mean(axis=0)
