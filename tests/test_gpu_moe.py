@@ -295,6 +295,47 @@ def test_prefill_small_layers(cfg, T):
     _check_layer(cfg, T, prefill=True)
 
 
+@pytest.mark.parametrize("cfg,T", [(PREFILL_TIERED, 300), (PREFILL_RAGGED, 260)])
+@pytest.mark.parametrize("prefill", [True, False])
+def test_partial_routing_writes_only_the_kept_rows(cfg, T, prefill):
+    """offsets[E] < T*k: the expert FFN (qgemm_grouped_prefill or
+    moe_ffn_tiered) on a routing that keeps only some experts' rows gives
+    those rows exactly as the full call does (each kept expert has the same
+    rows, so the same tiles) and leaves o[pos] for pos >= offsets[E]
+    untouched."""
+    layer = _layer(cfg)
+    _, xg = _x(cfg, T, seed=5)
+    _, ws = layer.forward(xg, prefill=prefill)
+    o_full = to_np(ws["o"]).copy()
+    offs = to_np(ws["offsets"]).astype(np.int64)
+    perm = to_np(ws["perm"])
+    cnt = np.diff(offs)
+    E, kt = cfg.E_total, cfg.k + cfg.n_shared
+    # every other expert in order of row count, and the busiest one
+    nz = np.nonzero(cnt > 0)[0]
+    nz = nz[np.argsort(cnt[nz], kind="stable")]
+    keep = np.zeros(E, bool)
+    keep[nz[0::2]] = True
+    keep[nz[-1]] = True
+    off2 = np.zeros(E + 1, np.int32)
+    off2[1:] = np.cumsum(np.where(keep, cnt, 0))
+    p2 = np.zeros(T * kt, np.int32)
+    p2[:off2[E]] = np.concatenate([perm[offs[e]:offs[e + 1]] for e in np.nonzero(keep)[0]])
+    o2 = torch.full_like(ws["o"], 12345.0)
+    L = qmoe.lib()
+    fn = L.qgemm_grouped_prefill if prefill else L.moe_ffn_tiered
+    arr = layer.tier_arrays[0]
+    off_t, p_t = to_gpu(off2), to_gpu(p2)
+    qmoe._check(fn(arr, len(arr), E, cfg.H, cfg.F, qmoe._p(xg), qmoe._dtype_code(xg), T, kt,
+                   qmoe._p(off_t), qmoe._p(p_t), qmoe._p(o2), qmoe._p(ws["ffn"]),
+                   ws["ffn"].numel(), qmoe._stream()), "expert ffn")
+    got = to_np(o2)
+    for e in np.nonzero(keep)[0]:
+        assert_bitexact(got[off2[e]:off2[e + 1]], o_full[offs[e]:offs[e + 1]],
+                        f"{cfg.name} prefill={prefill} expert {e}")
+    assert (got[off2[E]:] == 12345.0).all()
+
+
 def test_prefill_matches_decode_path():
     cfg = configs.TIERED
     layer = _layer(cfg)
